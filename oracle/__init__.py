@@ -1,0 +1,165 @@
+"""ctypes wrapper around the fp64 CPU oracle (oracle/oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg.  The GPU library never imports or links it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+FLAG_ACCEPT_NEAR, FLAG_CDF_NEAR, FLAG_TOPP_NEAR, FLAG_FALLBACK, FLAG_TOKEN_RANGE = 1, 2, 4, 8, 16
+FLAG_AMBIGUOUS = FLAG_ACCEPT_NEAR | FLAG_CDF_NEAR | FLAG_TOPP_NEAR
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with plain gcc: -O2, no fast-math, no OpenMP."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-std=c99", "-O2", "-fno-fast-math", "-fPIC",
+                               "-shared", "-o", tmp, SRC, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        D = ctypes.c_double
+        L.oracle_verify_sample.argtypes = [P, P, I, P, P, P, D, D, I, I, I, P, P, P, P, P, P, P]
+        L.oracle_verify_sample.restype = I
+        L.oracle_verify_greedy.argtypes = [P, I, P, I, I, I, P, P, P]
+        L.oracle_verify_greedy.restype = I
+        L.oracle_verify_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, P]
+        L.oracle_verify_tree.restype = I
+        L.oracle_row_distribution.argtypes = [P, I, I, D, D, P, P]
+        L.oracle_row_distribution.restype = I
+        L.oracle_tree_is_valid.argtypes = [P, P, I]
+        L.oracle_tree_is_valid.restype = I
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_code(arr: np.ndarray) -> int:
+    if arr.dtype == np.float32:
+        return F32
+    if arr.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"logits must be float32 or uint16 (bf16 bits), got {arr.dtype}")
+
+
+def row_distribution(logits: np.ndarray, temperature: float, top_p: float = 1.0):
+    """One row's tempered (and nucleus-filtered) distribution, fp64.
+    Returns (prob[V], info dict)."""
+    logits = np.ascontiguousarray(logits)
+    V = logits.shape[-1]
+    prob = np.empty(V, np.float64)
+    info = np.empty(7, np.float64)
+    rc = lib().oracle_row_distribution(_p(logits), _dtype_code(logits), V,
+                                       float(temperature), float(top_p), _p(prob), _p(info))
+    if rc != 0:
+        raise ValueError(f"oracle_row_distribution: {rc}")
+    return prob, dict(max=info[0], Z=info[1], kept=info[2], tau=info[3],
+                      before=info[4], after=info[5], cut_group=int(info[6]))
+
+
+def verify_sample(target, draft, tokens, u_accept, u_sample, temperature, top_p=1.0,
+                  row_info=False):
+    target = np.ascontiguousarray(target)
+    draft = np.ascontiguousarray(draft)
+    if draft.dtype != target.dtype:
+        raise TypeError("target and draft dtypes differ")
+    B, K1, V = target.shape
+    K = K1 - 1
+    assert draft.shape == (B, K, V)
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    ua = np.ascontiguousarray(u_accept, np.float32)
+    us = np.ascontiguousarray(u_sample, np.float32)
+    assert tokens.shape == (B, K) and ua.shape == (B, K) and us.shape == (B,)
+    out = dict(accepted=np.empty(B, np.int32), tokens=np.empty((B, K + 1), np.int32),
+               p=np.empty((B, K), np.float64), q=np.empty((B, K), np.float64),
+               S=np.empty(B, np.float64), flags=np.empty(B, np.int32))
+    info = np.empty((B, 2 * K + 1, 7), np.float64) if row_info else None
+    rc = lib().oracle_verify_sample(
+        _p(target), _p(draft), _dtype_code(target), _p(tokens), _p(ua), _p(us),
+        float(temperature), float(top_p), B, K, V, _p(out["accepted"]), _p(out["tokens"]),
+        _p(out["p"]), _p(out["q"]), _p(out["S"]), _p(out["flags"]), _p(info))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_sample: {rc}")
+    if row_info:
+        out["row_info"] = info
+    return out
+
+
+def verify_greedy(target, tokens):
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    assert tokens.shape == (B, K)
+    out = dict(accepted=np.empty(B, np.int32), tokens=np.empty((B, K + 1), np.int32),
+               argmax=np.empty((B, K + 1), np.int32))
+    rc = lib().oracle_verify_greedy(_p(target), _dtype_code(target), _p(tokens), B, K, V,
+                                    _p(out["accepted"]), _p(out["tokens"]), _p(out["argmax"]))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_greedy: {rc}")
+    return out
+
+
+def verify_tree(target, parents, node_tokens, anc_mask):
+    target = np.ascontiguousarray(target)
+    B, N, V = target.shape
+    parents = np.ascontiguousarray(parents, np.int32)
+    node_tokens = np.ascontiguousarray(node_tokens, np.int32)
+    anc_mask = np.ascontiguousarray(anc_mask, np.uint8)
+    assert parents.shape == (B, N) and node_tokens.shape == (B, N)
+    assert anc_mask.shape == (B, N, N)
+    out = dict(path_len=np.empty(B, np.int32), path_nodes=np.empty((B, N), np.int32),
+               tokens=np.empty((B, N), np.int32), valid=np.empty(B, np.int32),
+               argmax=np.empty((B, N), np.int32))
+    rc = lib().oracle_verify_tree(_p(target), _dtype_code(target), _p(parents),
+                                  _p(node_tokens), _p(anc_mask), B, N, V,
+                                  _p(out["path_len"]), _p(out["path_nodes"]),
+                                  _p(out["tokens"]), _p(out["valid"]), _p(out["argmax"]))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree: {rc}")
+    return out
+
+
+def tree_is_valid(parents, anc_mask) -> bool:
+    parents = np.ascontiguousarray(parents, np.int32)
+    anc_mask = np.ascontiguousarray(anc_mask, np.uint8)
+    N = parents.shape[0]
+    rc = lib().oracle_tree_is_valid(_p(parents), _p(anc_mask), N)
+    if rc < 0:
+        raise ValueError("oracle_tree_is_valid: bad arguments")
+    return bool(rc)
+
+
+def verify_workload(w):
+    """Run the oracle on a workloads.Workload."""
+    if w.kind == "sample":
+        return verify_sample(w.target, w.draft, w.tokens, w.u_accept, w.u_sample,
+                             w.temperature, w.top_p)
+    if w.kind == "greedy":
+        return verify_greedy(w.target, w.tokens)
+    return verify_tree(w.target, w.parents, w.tokens, w.anc_mask)
