@@ -49,6 +49,8 @@
 #define FLAG_TOPP_NEAR 4     /* an alternative nucleus near top_p changes the output */
 #define FLAG_FALLBACK 8      /* residual mass S <= 0, drew from p' instead */
 #define FLAG_TOKEN_RANGE 16  /* a draft token outside [0, V) */
+#define FLAG_TOPP_EDGE 32    /* some row's nucleus edge lies within 1e-6 of top_p
+                                (informational: p', q' may legitimately differ) */
 
 #define REL_TOL 1e-6
 
@@ -324,6 +326,7 @@ int oracle_verify_sample(const void *target, const void *draft, int dtype,
         int shifts[2] = {0, 0};
         if (infos[row][6] > 0.0 && fabs(before - top_p) <= REL_TOL) shifts[0] = -1;
         if (fabs(after - top_p) <= REL_TOL) shifts[1] = +1;
+        if (shifts[0] || shifts[1]) res.flags |= FLAG_TOPP_EDGE;
         for (int s = 0; s < 2; ++s) {
           if (!shifts[s]) continue;
           SampleResult alt = verify_one_request(tb, db, dtype, tok, ua, u_sample[b], T,

@@ -1,0 +1,239 @@
+// extern "C" entry points of libspecverify.so (declared in include/spec_verify.h).
+// Every argument is validated on the host before the first HIP call, so an
+// invalid call returns an error code with nothing enqueued.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "spec_verify.h"
+#include "sv_kernels.hpp"
+#include "sv_layout.hpp"
+
+namespace {
+
+using sv::Layout;
+using sv::Scale;
+
+constexpr int kMaxK = 63;
+constexpr int kMaxN = 64;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// log2(e) / T split into float hi + lo with lo > 0 (lo carries the rounding
+// of hi, so the product (l - m) * k keeps ~1 ulp accuracy per element).
+Scale make_scale(double k64) {
+  float hi = (float)k64;
+  if ((double)hi >= k64) hi = std::nextafter(hi, 0.0f);
+  float lo = (float)(k64 - (double)hi);
+  if (!(lo > 0.0f)) {
+    hi = std::nextafter(hi, 0.0f);
+    lo = (float)(k64 - (double)hi);
+  }
+  return Scale{hi, lo};
+}
+
+int check_shape(long B, long KN, long V, int op) {
+  if (B < 1 || V < 1 || V > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
+  if (op == SPEC_OP_TREE) {
+    if (KN < 1 || KN > kMaxN) return SPEC_ERR_SHAPE;
+  } else if (KN < 1 || KN > kMaxK) {
+    return SPEC_ERR_SHAPE;
+  }
+  // one workgroup per (row, split) on a 1-D grid
+  const long rows = op == SPEC_OP_SAMPLE ? B * (2 * KN + 1) : op == SPEC_OP_GREEDY ? B * (KN + 1) : B * KN;
+  if (B > 0x7FFFFFFFL || rows > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
+  const long S = sv::num_splits((int)V, SPEC_F32);  // the f32 split count is the larger one
+  if (rows * S > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
+  return SPEC_OK;
+}
+
+bool dtype_ok(int dtype) { return dtype == SPEC_F32 || dtype == SPEC_BF16; }
+
+int check_workspace(void *ws, size_t bytes, const Layout &L) {
+  if (L.total > 0 && !ws) return SPEC_ERR_NULL;
+  if (!aligned(ws, 256)) return SPEC_ERR_ALIGN;
+  if (bytes < L.total) return SPEC_ERR_WORKSPACE;
+  return SPEC_OK;
+}
+
+template <class T>
+T *carve(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+// ---- profiling hook: events around the logit-streaming kernel ----
+struct Profile {
+  bool active = false;
+  int max = 0;
+  std::vector<hipEvent_t> ev;  // pairs
+  int used = 0;
+} g_prof;
+
+void prof_before(hipStream_t s) {
+  if (g_prof.active && g_prof.used < g_prof.max) (void)hipEventRecord(g_prof.ev[2 * g_prof.used], s);
+}
+void prof_after(hipStream_t s) {
+  if (g_prof.active && g_prof.used < g_prof.max) {
+    (void)hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
+    ++g_prof.used;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_bytes(int op, int B, int K_or_N, int V, int dtype, int use_top_p) {
+  if (op != SPEC_OP_GREEDY && op != SPEC_OP_SAMPLE && op != SPEC_OP_TREE) return 0;
+  if (!dtype_ok(dtype) || check_shape(B, K_or_N, V, op) != SPEC_OK) return 0;
+  return sv::make_layout(op, B, K_or_N, V, dtype, use_top_p ? 1 : 0).total;
+}
+
+const char *spec_status_string(int status) {
+  switch (status) {
+    case SPEC_OK: return "ok";
+    case SPEC_ERR_NULL: return "a required pointer is NULL";
+    case SPEC_ERR_SHAPE: return "B, K, N or V out of range";
+    case SPEC_ERR_PARAM: return "bad temperature, top_p, dtype or op";
+    case SPEC_ERR_WORKSPACE: return "workspace too small";
+    case SPEC_ERR_ALIGN: return "misaligned workspace or logits";
+    case SPEC_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draft_tokens, int B,
+                       int K, int V, int32_t *out_accepted, int32_t *out_tokens, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (!target_logits || !draft_tokens || !out_accepted || !out_tokens) return SPEC_ERR_NULL;
+  if (!dtype_ok(dtype)) return SPEC_ERR_PARAM;
+  int rc = check_shape(B, K, V, SPEC_OP_GREEDY);
+  if (rc) return rc;
+  if (!aligned(target_logits, sv::elem_bytes(dtype))) return SPEC_ERR_ALIGN;
+  const Layout L = sv::make_layout(SPEC_OP_GREEDY, B, K, V, dtype, 0);
+  if ((rc = check_workspace(workspace, workspace_bytes, L))) return rc;
+  uint64_t *part_key = carve<uint64_t>(workspace, L.part_key);
+  prof_before(stream);
+  if (sv::launch_argmax_partial(target_logits, dtype, B * (K + 1), V, L.S, part_key, stream) !=
+      hipSuccess)
+    return SPEC_ERR_HIP;
+  prof_after(stream);
+  if (sv::launch_greedy_decide(draft_tokens, B, K, L.S, part_key, out_accepted, out_tokens,
+                               stream) != hipSuccess)
+    return SPEC_ERR_HIP;
+  return SPEC_OK;
+}
+
+int spec_verify_sample(const void *target_logits, const void *draft_logits, int dtype,
+                       const int32_t *draft_tokens, const float *u_accept,
+                       const float *u_sample, float temperature, float top_p, int B, int K,
+                       int V, int32_t *out_accepted, int32_t *out_tokens, float *out_p_draft,
+                       float *out_q_draft, float *out_residual_mass, void *workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_sample ||
+      !out_accepted || !out_tokens)
+    return SPEC_ERR_NULL;
+  if (!dtype_ok(dtype)) return SPEC_ERR_PARAM;
+  if (!std::isfinite(temperature) || !(temperature > 0.0f)) return SPEC_ERR_PARAM;
+  if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return SPEC_ERR_PARAM;
+  int rc = check_shape(B, K, V, SPEC_OP_SAMPLE);
+  if (rc) return rc;
+  if (!aligned(target_logits, sv::elem_bytes(dtype)) || !aligned(draft_logits, sv::elem_bytes(dtype)))
+    return SPEC_ERR_ALIGN;
+  const double k64 = 1.4426950408889634 / (double)temperature;  // log2(e) / T
+  if (!std::isfinite(k64) || !(k64 > 0.0) || k64 > 3.0e38) return SPEC_ERR_PARAM;
+  const int use_top_p = top_p < 1.0f;
+  const Layout L = sv::make_layout(SPEC_OP_SAMPLE, B, K, V, dtype, use_top_p);
+  if ((rc = check_workspace(workspace, workspace_bytes, L))) return rc;
+  const Scale k = make_scale(k64);
+  float *part_m = carve<float>(workspace, L.part_m);
+  double *part_z = carve<double>(workspace, L.part_z);
+  sv::RowStat *rowstat = use_top_p ? carve<sv::RowStat>(workspace, L.rowstat) : nullptr;
+  sv::Decision *dec = carve<sv::Decision>(workspace, L.decision);
+  sv::ResidPart *rpart = carve<sv::ResidPart>(workspace, L.rpart);
+  const int rows_t = B * (K + 1), rows_d = B * K;
+
+  prof_before(stream);
+  if (sv::launch_softmax_partial(target_logits, draft_logits, dtype, rows_t, rows_d, V, L.S, k,
+                                 part_m, part_z, stream) != hipSuccess)
+    return SPEC_ERR_HIP;
+  prof_after(stream);
+  if (use_top_p &&
+      sv::launch_topp_select(target_logits, draft_logits, dtype, rows_t, rows_d, V, L.S, k, k64,
+                             (double)top_p, part_m, part_z, rowstat, stream) != hipSuccess)
+    return SPEC_ERR_HIP;
+  if (sv::launch_sample_decide(target_logits, draft_logits, dtype, draft_tokens, u_accept, B, K,
+                               V, L.S, k64, part_m, part_z, rowstat, out_accepted, out_tokens,
+                               out_p_draft, out_q_draft, dec, stream) != hipSuccess)
+    return SPEC_ERR_HIP;
+  if (sv::launch_resid_partial(target_logits, draft_logits, dtype, B, K, V, L.S, k, dec, rpart,
+                               stream) != hipSuccess)
+    return SPEC_ERR_HIP;
+  if (sv::launch_sample_locate(target_logits, draft_logits, dtype, u_sample, B, K, V, L.S, k,
+                               dec, rpart, out_tokens, out_residual_mass, stream) != hipSuccess)
+    return SPEC_ERR_HIP;
+  return SPEC_OK;
+}
+
+int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parents,
+                     const int32_t *node_tokens, const uint8_t *anc_mask, int B, int N, int V,
+                     int32_t *out_path_len, int32_t *out_path_nodes, int32_t *out_tokens,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!target_logits || !parents || !node_tokens || !anc_mask || !out_path_len ||
+      !out_path_nodes || !out_tokens)
+    return SPEC_ERR_NULL;
+  if (!dtype_ok(dtype)) return SPEC_ERR_PARAM;
+  int rc = check_shape(B, N, V, SPEC_OP_TREE);
+  if (rc) return rc;
+  if (!aligned(target_logits, sv::elem_bytes(dtype))) return SPEC_ERR_ALIGN;
+  const Layout L = sv::make_layout(SPEC_OP_TREE, B, N, V, dtype, 0);
+  if ((rc = check_workspace(workspace, workspace_bytes, L))) return rc;
+  uint64_t *part_key = carve<uint64_t>(workspace, L.part_key);
+  prof_before(stream);
+  if (sv::launch_argmax_partial(target_logits, dtype, B * N, V, L.S, part_key, stream) !=
+      hipSuccess)
+    return SPEC_ERR_HIP;
+  prof_after(stream);
+  if (sv::launch_tree_decide(parents, node_tokens, anc_mask, B, N, L.S, part_key, out_path_len,
+                             out_path_nodes, out_tokens, stream) != hipSuccess)
+    return SPEC_ERR_HIP;
+  return SPEC_OK;
+}
+
+int spec_profile_begin(int max_launches) {
+  if (max_launches < 1 || max_launches > (1 << 20)) return SPEC_ERR_PARAM;
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  for (auto &e : g_prof.ev)
+    if (hipEventCreate(&e) != hipSuccess) return SPEC_ERR_HIP;
+  g_prof.max = max_launches;
+  g_prof.used = 0;
+  g_prof.active = true;
+  return SPEC_OK;
+}
+
+int spec_profile_end(double *total_ms, int *launches) {
+  if (!total_ms || !launches) return SPEC_ERR_NULL;
+  double sum = 0.0;
+  int rc = SPEC_OK;
+  for (int i = 0; i < g_prof.used; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) {
+      rc = SPEC_ERR_HIP;
+      break;
+    }
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = g_prof.used;
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.active = false;
+  g_prof.used = 0;
+  g_prof.max = 0;
+  return rc;
+}
+
+}  // extern "C"

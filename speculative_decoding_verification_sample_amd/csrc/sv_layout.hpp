@@ -1,0 +1,96 @@
+// Shared host/device constants, workspace records and the workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// Streaming geometry: a workgroup of 256 lanes streams one split of one row,
+// each lane holding 8 16-byte loads in flight (32 KB per workgroup).
+constexpr int kThreads = 256;
+constexpr int kVecPerThread = 8;
+
+__host__ __device__ constexpr int elem_bytes(int dtype) { return dtype == kBF16 ? 2 : 4; }
+__host__ __device__ constexpr int split_elems(int dtype) {
+  return kThreads * kVecPerThread * (16 / elem_bytes(dtype));
+}
+__host__ __device__ inline int num_splits(int V, int dtype) {
+  return (V + split_elems(dtype) - 1) / split_elems(dtype);
+}
+
+// k = log2(e) / T as an unevaluated sum hi + lo of two floats, lo > 0.
+struct Scale {
+  float hi, lo;
+};
+
+// One row's softmax statistics after combining its splits (and top-p).
+struct RowStat {
+  double z;   // sum over the row of 2^((l - m) k)
+  double zk;  // kept (nucleus) mass in the same units; == z without top-p
+  float m;    // row maximum
+  float tau;  // smallest kept logit; -inf keeps everything
+};
+
+// Per request, written by the decide kernel for the resample kernels.
+struct Decision {
+  int n;        // accepted drafts (0..K)
+  int mode;     // kModeResidual or kModeBonus
+  float m_t, tau_t, m_d, tau_d;
+  double inv_t, inv_d;  // 1 / kept mass of target row n / draft row n
+};
+constexpr int kModeResidual = 0;
+constexpr int kModeBonus = 1;
+
+// Per (request, split) partial sums for the inverse-CDF draw.
+struct ResidPart {
+  double r;    // sum of max(0, p' - q') (bonus: p')
+  double p;    // sum of p' (used if the residual mass is not positive)
+  int last_r;  // last element with r > 0, -1 if none
+  int last_p;  // last element with p' > 0, -1 if none
+};
+
+struct Layout {
+  int S = 0;       // splits per row
+  int rows = 0;    // logit rows streamed
+  size_t part_m = 0, part_z = 0, part_key = 0, rowstat = 0, decision = 0, rpart = 0;
+  size_t total = 0;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// op: 0 greedy, 1 sample, 2 tree.  KN = K (greedy/sample) or N (tree).
+inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p) {
+  Layout L;
+  L.S = num_splits(V, dtype);
+  if (op == 1)
+    L.rows = B * (2 * KN + 1);
+  else if (op == 0)
+    L.rows = B * (KN + 1);
+  else
+    L.rows = B * KN;
+  size_t cells = (size_t)L.rows * (size_t)L.S;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  if (op == 1) {
+    L.part_m = take(cells * sizeof(float));
+    L.part_z = take(cells * sizeof(double));
+    L.rowstat = use_top_p ? take((size_t)L.rows * sizeof(RowStat)) : 0;
+    L.decision = take((size_t)B * sizeof(Decision));
+    L.rpart = take((size_t)B * (size_t)L.S * sizeof(ResidPart));
+  } else {
+    L.part_key = take(cells * sizeof(uint64_t));
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace sv

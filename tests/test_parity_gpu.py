@@ -1,0 +1,196 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on
+identical seeded inputs.  Bit-exact accepted lengths and tokens except on
+requests the oracle flags (a uniform within 1e-6 relative of a threshold or
+CDF step, or a nucleus edge whose alternative changes the output);
+probabilities and residual masses within 1e-5 absolute."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity import (check_greedy, check_sample, check_tree, host, run_workload, say, subset,
+                    to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _check(w, offset=0, **kw):
+    say(f"case: {w.name} kind={w.kind} B={w.B} K={w.K} V={w.V} {w.dtype} "
+        f"T={w.temperature} top_p={w.top_p} offset={offset}")
+    got = run_workload(w, offset, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.verify_workload(w)
+    if w.kind == "sample":
+        flagged = check_sample(w, got, ref)
+        say(f"  flagged {flagged}/{w.B}, mean accepted {ref['accepted'].mean():.2f}")
+    elif w.kind == "greedy":
+        check_greedy(w, got, ref)
+    else:
+        check_tree(w, got, ref)
+    return got, ref
+
+
+# ---------------------------------------------------------------------------
+# the five settings at reduced B / V (several splits and a ragged tail)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,kw", [
+    (0, dict()),                      # c1 at full size
+    (1, dict(B=8, V=70001)),
+    (2, dict(B=8, V=50003)),
+    (3, dict(B=6, V=30011)),
+    (4, dict(B=6, V=20011)),
+])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_configs_reduced(cfg, kw, seed):
+    _check(W.make_config(cfg, seed=seed, **kw))
+
+
+# ---------------------------------------------------------------------------
+# full sizes, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+def test_full_c2_greedy():
+    _check(W.make_config(1))
+
+
+def test_full_c3_sample():
+    _check(W.make_config(2))
+
+
+def test_full_c5_tree():
+    _check(W.make_config(4))
+
+
+def test_full_c4_topp_sampled_requests():
+    """B=256 on the GPU; the oracle recomputes 12 requests one by one."""
+    w = W.make_config(3)
+    say(f"case: full c4 B={w.B} K={w.K} V={w.V}")
+    got = run_workload(w)
+    torch.cuda.synchronize()
+    reqs = np.random.default_rng(7).choice(w.B, size=12, replace=False)
+    ref = oracle.verify_workload(subset(w, reqs))
+    flagged = check_sample(w, got, ref, requests=reqs)
+    say(f"  flagged {flagged}/12")
+
+
+# ---------------------------------------------------------------------------
+# shape fuzz, alignment, dtypes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V", [1, 2, 7, 8, 9, 4097, 16385, 32769])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fuzz_sample(V, dtype):
+    for B, K in ((1, 1), (3, 2), (3, 7)):
+        w = W.sample_gaussian(10, B, K, V, dtype, 2.0, 1.0, 0.9, seed=V + K, name="fuzz")
+        for off in (0, 1):
+            _check(w, offset=off)
+        wp = W.sample_gaussian(11, B, K, V, dtype, 2.0, 1.0, 0.9, seed=V + K, name="fuzz-topp")
+        wp.top_p = float(np.float32(0.8))
+        _check(wp, offset=1)
+
+
+@pytest.mark.parametrize("V", [1, 2, 7, 9, 4097, 32769])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fuzz_greedy_and_tree(V, dtype):
+    for B, K in ((1, 1), (3, 2), (2, 7)):
+        w = W.greedy_gaussian(12, B, K, V, dtype, seed=V + K, name="fuzz-greedy")
+        for off in (0, 1):
+            _check(w, offset=off)
+    for n in (0, 1, 3):
+        w = W.tree_merged(13, 2, n, V, dtype, seed=V + n, name="fuzz-tree")
+        _check(w, offset=1)
+
+
+def test_max_sizes_k63_n64():
+    w = W.sample_gaussian(14, 2, 63, 3001, "bf16", 1.0, 0.1, 1.0, name="K63")
+    _check(w)
+    g = W.greedy_gaussian(15, 2, 63, 3001, "f32", agree=0.97, name="greedy-K63")
+    _check(g)
+    # N = 64: a chain of 64 nodes (the greedy path through every node)
+    B, N, V = 2, 64, 777
+    t = W.greedy_gaussian(16, B, N - 1, V, "bf16", agree=1.0, name="chain64")
+    parents = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    node_tokens = np.concatenate([np.zeros((B, 1), np.int32), t.tokens], axis=1)
+    mask = np.tile(np.tril(np.ones((N, N), np.uint8)), (B, 1, 1))
+    tw = W.Workload("tree", "chain64", B, N, V, "bf16", t.target, tokens=node_tokens,
+                    parents=parents, anc_mask=mask)
+    got, ref = _check(tw)
+    assert (ref["path_len"] == N - 1).all()
+
+
+# ---------------------------------------------------------------------------
+# ties, -inf entries, degenerate distributions
+# ---------------------------------------------------------------------------
+
+def test_topp_with_tie_groups():
+    """Quantised logits (few distinct values): nucleus edges fall inside big
+    tie groups, and whole groups must be kept."""
+    rng = np.random.default_rng(3)
+    B, K, V = 4, 3, 5000
+    t32 = np.round(rng.normal(0, 2, (B, K + 1, V))).astype(np.float32)
+    d32 = np.round(t32[:, :K] + rng.normal(0, 1, (B, K, V))).astype(np.float32)
+    for dtype in ("f32", "bf16"):
+        tgt = W.f32_to_bf16_bits(t32) if dtype == "bf16" else t32
+        dft = W.f32_to_bf16_bits(d32) if dtype == "bf16" else d32
+        toks = W.drafter_tokens(W.logits_as_f32(dft, dtype), 1.0, 1.0, rng)
+        for top_p in (0.3, 0.9, 0.999):
+            w = W.Workload("sample", f"ties p={top_p}", B, K, V, dtype, tgt, dft, toks,
+                           W.uniforms_on_grid(rng, (B, K)), W.uniforms_on_grid(rng, (B,)),
+                           1.0, float(np.float32(top_p)))
+            _check(w)
+
+
+def test_flat_rows_and_neg_inf():
+    rng = np.random.default_rng(4)
+    B, K, V = 4, 3, 3000
+    t32 = np.zeros((B, K + 1, V), np.float32)                # flat target rows
+    d32 = rng.normal(0, 1, (B, K, V)).astype(np.float32)
+    d32[rng.random(d32.shape) < 0.3] = -np.inf                 # masked draft entries
+    t32[1, :, :V // 2] = -np.inf                               # half-masked target rows
+    toks = W.drafter_tokens(d32, 1.0, 1.0, rng)
+    for top_p in (1.0, 0.5):
+        w = W.Workload("sample", f"flat/-inf p={top_p}", B, K, V, "f32", t32, d32, toks,
+                       W.uniforms_on_grid(rng, (B, K)), W.uniforms_on_grid(rng, (B,)), 1.0,
+                       float(np.float32(top_p)))
+        _check(w)
+    g = W.Workload("greedy", "flat greedy", B, K, V, "f32", t32, tokens=toks)
+    _check(g)
+
+
+def test_out_of_range_tokens_and_equal_distributions():
+    w = W.make_config(2, B=6, V=9001)
+    w.tokens = w.tokens.copy()
+    w.tokens[0, 0] = -3
+    w.tokens[1, 2] = w.V
+    _check(w)
+    # p == q: every draft accepted, bonus from the last target row
+    e = W.make_config(2, B=6, V=9001, seed=5)
+    e.draft = e.target[:, :e.K].copy()
+    e.tokens = W.drafter_tokens(W.logits_as_f32(e.draft, "bf16"), e.temperature, 1.0,
+                                np.random.default_rng(1))
+    got, ref = _check(e)
+    assert (host(got["accepted"]) == e.K).all()
+
+
+# ---------------------------------------------------------------------------
+# determinism and workspace reuse
+# ---------------------------------------------------------------------------
+
+def test_run_twice_bit_identical_with_poisoned_workspace():
+    import speculative_decoding_verification_sample_amd as sv
+    w = W.make_config(3, B=4, V=20011)
+    nbytes = sv.verify_workspace_bytes(sv.SPEC_OP_SAMPLE, w.B, w.K, w.V, sv.SPEC_F32, True)
+    ws = torch.full((nbytes + 256,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    args = (to_dev(w.target), to_dev(w.draft), to_dev(w.tokens), to_dev(w.u_accept),
+            to_dev(w.u_sample), w.temperature, w.top_p)
+    a = sv.verify_sample(*args, workspace=ws)
+    ws.fill_(0x7F)
+    b = sv.verify_sample(*args, workspace=ws)
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+    ref = oracle.verify_workload(w)
+    check_sample(w, a, ref)
