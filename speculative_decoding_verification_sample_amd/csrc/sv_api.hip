@@ -1,6 +1,8 @@
 // extern "C" entry points of libspecverify.so (declared in include/spec_verify.h).
 // Every argument is validated on the host before the first HIP call, so an
 // invalid call returns an error code with nothing enqueued.
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -45,7 +47,23 @@ int check_shape(long B, long KN, long V, int op) {
   if (B > 0x7FFFFFFFL || rows > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
   const long S = sv::num_splits((int)V, SPEC_F32);  // the f32 split count is the larger one
   if (rows * S > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
+  if (op == SPEC_OP_SAMPLE && B * (long)sv::num_splits_b((int)V, SPEC_F32) + rows * S > 0x7FFFFFFFL)
+    return SPEC_ERR_SHAPE;
+  // the draw stages a request's residual splits in LDS
+  if (op == SPEC_OP_SAMPLE && sv::num_splits_b((int)V, SPEC_F32) > sv::kMaxSplitsB)
+    return SPEC_ERR_SHAPE;
   return SPEC_OK;
+}
+
+// Every call tags its partials with a fresh 64-bit epoch.  The sequence
+// starts from a scrambled clock reading so that tags left in reused memory by
+// another process do not match.
+std::atomic<uint64_t> g_epoch{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() *
+                              0x9E3779B97F4A7C15ull};
+
+sv::u64 next_epoch() {
+  sv::u64 e = g_epoch.fetch_add(0x9E3779B97F4A7C15ull);
+  return e ? e : 1;
 }
 
 bool dtype_ok(int dtype) { return dtype == SPEC_F32 || dtype == SPEC_BF16; }
@@ -114,14 +132,12 @@ int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draf
   const Layout L = sv::make_layout(SPEC_OP_GREEDY, B, K, V, dtype, 0);
   if ((rc = check_workspace(workspace, workspace_bytes, L))) return rc;
   uint64_t *part_key = carve<uint64_t>(workspace, L.part_key);
+  sv::u64 *part_tag = carve<sv::u64>(workspace, L.part_tag);
   prof_before(stream);
-  if (sv::launch_argmax_partial(target_logits, dtype, B * (K + 1), V, L.S, part_key, stream) !=
-      hipSuccess)
+  if (sv::launch_greedy(target_logits, dtype, draft_tokens, B, K, V, L.S, next_epoch(), part_key,
+                        part_tag, out_accepted, out_tokens, stream) != hipSuccess)
     return SPEC_ERR_HIP;
   prof_after(stream);
-  if (sv::launch_greedy_decide(draft_tokens, B, K, L.S, part_key, out_accepted, out_tokens,
-                               stream) != hipSuccess)
-    return SPEC_ERR_HIP;
   return SPEC_OK;
 }
 
@@ -147,32 +163,27 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   const Layout L = sv::make_layout(SPEC_OP_SAMPLE, B, K, V, dtype, use_top_p);
   if ((rc = check_workspace(workspace, workspace_bytes, L))) return rc;
   const Scale k = make_scale(k64);
-  float *part_m = carve<float>(workspace, L.part_m);
-  double *part_z = carve<double>(workspace, L.part_z);
+  sv::u64 *part_m = carve<sv::u64>(workspace, L.part_m);
+  sv::u64 *part_z = carve<sv::u64>(workspace, L.part_z);
   sv::RowStat *rowstat = use_top_p ? carve<sv::RowStat>(workspace, L.rowstat) : nullptr;
-  sv::Decision *dec = carve<sv::Decision>(workspace, L.decision);
   sv::ResidPart *rpart = carve<sv::ResidPart>(workspace, L.rpart);
   const int rows_t = B * (K + 1), rows_d = B * K;
-
+  const sv::u64 epoch = next_epoch();
+  auto run = [&](int phase) {
+    return sv::launch_sample(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample,
+                             B, K, V, L.S, L.SB, k64, k, epoch, phase, part_m, part_z, rowstat,
+                             rpart, out_accepted, out_tokens, out_p_draft,
+                             out_q_draft, out_residual_mass, stream);
+  };
   prof_before(stream);
-  if (sv::launch_softmax_partial(target_logits, draft_logits, dtype, rows_t, rows_d, V, L.S, k,
-                                 part_m, part_z, stream) != hipSuccess)
-    return SPEC_ERR_HIP;
+  if (run(use_top_p ? 1 : 0) != hipSuccess) return SPEC_ERR_HIP;
   prof_after(stream);
-  if (use_top_p &&
-      sv::launch_topp_select(target_logits, draft_logits, dtype, rows_t, rows_d, V, L.S, k, k64,
-                             (double)top_p, part_m, part_z, rowstat, stream) != hipSuccess)
-    return SPEC_ERR_HIP;
-  if (sv::launch_sample_decide(target_logits, draft_logits, dtype, draft_tokens, u_accept, B, K,
-                               V, L.S, k64, part_m, part_z, rowstat, out_accepted, out_tokens,
-                               out_p_draft, out_q_draft, dec, stream) != hipSuccess)
-    return SPEC_ERR_HIP;
-  if (sv::launch_resid_partial(target_logits, draft_logits, dtype, B, K, V, L.S, k, dec, rpart,
-                               stream) != hipSuccess)
-    return SPEC_ERR_HIP;
-  if (sv::launch_sample_locate(target_logits, draft_logits, dtype, u_sample, B, K, V, L.S, k,
-                               dec, rpart, out_tokens, out_residual_mass, stream) != hipSuccess)
-    return SPEC_ERR_HIP;
+  if (use_top_p) {
+    if (sv::launch_topp_select(target_logits, draft_logits, dtype, rows_t, rows_d, V, L.S, k, k64,
+                               (double)top_p, part_m, part_z, rowstat, stream) != hipSuccess)
+      return SPEC_ERR_HIP;
+    if (run(2) != hipSuccess) return SPEC_ERR_HIP;
+  }
   return SPEC_OK;
 }
 
@@ -190,14 +201,13 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parent
   const Layout L = sv::make_layout(SPEC_OP_TREE, B, N, V, dtype, 0);
   if ((rc = check_workspace(workspace, workspace_bytes, L))) return rc;
   uint64_t *part_key = carve<uint64_t>(workspace, L.part_key);
+  sv::u64 *part_tag = carve<sv::u64>(workspace, L.part_tag);
   prof_before(stream);
-  if (sv::launch_argmax_partial(target_logits, dtype, B * N, V, L.S, part_key, stream) !=
-      hipSuccess)
+  if (sv::launch_tree(target_logits, dtype, parents, node_tokens, anc_mask, B, N, V, L.S,
+                      next_epoch(), part_key, part_tag, out_path_len, out_path_nodes, out_tokens,
+                      stream) != hipSuccess)
     return SPEC_ERR_HIP;
   prof_after(stream);
-  if (sv::launch_tree_decide(parents, node_tokens, anc_mask, B, N, L.S, part_key, out_path_len,
-                             out_path_nodes, out_tokens, stream) != hipSuccess)
-    return SPEC_ERR_HIP;
   return SPEC_OK;
 }
 

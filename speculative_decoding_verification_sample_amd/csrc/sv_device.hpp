@@ -56,6 +56,28 @@ __device__ __forceinline__ const u32x4 *span_body(const Span &sp, int dtype) {
   return reinterpret_cast<const u32x4 *>(sp.base + (size_t)sp.head * elem_bytes(dtype));
 }
 
+// Generic split geometry: `per` elements per split (a multiple of 8).
+__device__ __forceinline__ Span split_span_n(const char *row, int V, int s, int per, int dtype) {
+  const int es = elem_bytes(dtype);
+  const int epv = 16 / es;
+  Span sp;
+  sp.e0 = s * per;
+  const int e1 = min(V, sp.e0 + per);
+  sp.n = max(0, e1 - sp.e0);
+  sp.base = row + (size_t)sp.e0 * es;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(sp.base);
+  const int head = (int)(((16u - (unsigned)(a & 15u)) & 15u) / (unsigned)es);
+  sp.head = min(head, sp.n);
+  const int rest = sp.n - sp.head;
+  sp.nvec = rest / epv;
+  sp.tail = rest - sp.nvec * epv;
+  return sp;
+}
+
+__device__ __forceinline__ u32x4 load_stream(const u32x4 *p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // ---------------------------------------------------------------------------
 // element access
 // ---------------------------------------------------------------------------
@@ -135,5 +157,100 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---------------------------------------------------------------------------
+// cross-workgroup hand-off without whole-cache fences.  The 8 XCDs have their
+// own L2s; an agent-scope fence writes back and invalidates a whole L2.
+// Instead the few words that one workgroup hands to another are stored and
+// loaded as agent-scope relaxed atomics (coherent across XCDs), and the
+// producer waits for its stores to complete before it bumps the counter.
+// ---------------------------------------------------------------------------
+
+template <class T>
+__device__ __forceinline__ void store_agent(T *p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class T>
+__device__ __forceinline__ T load_agent(const T *p) {
+  return __hip_atomic_load(const_cast<T *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every memory operation this lane issued has completed.
+__device__ __forceinline__ void wait_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Epoch tags.  Every call carries a fresh 64-bit epoch.  A producer stores
+// its partial, waits for those stores to complete, then stores the epoch in
+// the partial's tag word; a consumer polls the tags of the cells it needs
+// and reads a cell only once its tag equals the current epoch.  Tags left by
+// earlier calls (or whatever the workspace held) never match, so nothing has
+// to clear the workspace, and no atomic read-modify-write is involved.
+__device__ __forceinline__ void publish_tag(u64 *tag, u64 epoch) {
+  wait_memory();  // the partial's stores are complete before the tag lands
+  store_agent(tag, epoch);
+}
+
+// Bounded wait (about a second at most) until *tag == epoch; false on
+// time-out.  Only ever used on work that has already been dispatched.
+constexpr int kSpinLimit = 1 << 20;
+__device__ __forceinline__ bool tag_wait(const u64 *tag, u64 epoch) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    if (load_agent(tag) == epoch) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+
+// The whole workgroup waits for tags[0..n); false if any wait timed out.
+__device__ __forceinline__ bool block_wait_tags(const u64 *tags, int n, u64 epoch, int *flag) {
+  if (threadIdx.x == 0) *flag = 1;
+  __syncthreads();
+  bool ok = true;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ok = ok && tag_wait(&tags[i], epoch);
+  if (!ok) *flag = 0;
+  __syncthreads();
+  return *flag != 0;
+}
+
+// Self-validating 64-bit words: the epoch's bits ride in the low bits of
+// each word, so one store publishes a value and one load both reads and
+// validates it (no store-completion wait, no separate tag round trip).
+//  - an fp32 value widened to fp64 has 29 zero low bits: 24 carry tag bits
+//    and clearing them restores the value exactly;
+//  - an fp64 value gives up its low 16 bits (a relative change below 2^-36;
+//    zero stays exactly zero).
+__device__ __forceinline__ u64 tag24(u64 epoch) { return epoch & 0xFFFFFFull; }
+__device__ __forceinline__ u64 tag16(u64 epoch) { return (epoch >> 24) & 0xFFFFull; }
+
+__device__ __forceinline__ u64 pack_f32(float v, u64 epoch) {
+  return ((u64)__double_as_longlong((double)v) & ~0xFFFFFFull) | tag24(epoch);
+}
+__device__ __forceinline__ bool unpack_f32(u64 w, u64 epoch, float *v) {
+  *v = (float)__longlong_as_double((long long)(w & ~0xFFFFFFull));
+  return (w & 0xFFFFFFull) == tag24(epoch);
+}
+__device__ __forceinline__ u64 pack_f64(double v, u64 epoch) {
+  return ((u64)__double_as_longlong(v) & ~0xFFFFull) | tag16(epoch);
+}
+__device__ __forceinline__ bool unpack_f64(u64 w, u64 epoch, double *v) {
+  // clear the tag bits: 0.0 must decode as exactly 0.0 (not a denormal)
+  *v = __longlong_as_double((long long)(w & ~0xFFFFull));
+  return (w & 0xFFFFull) == tag16(epoch);
+}
+// two 16-bit indices (each -1 .. 65534) and the epoch's low 32 bits
+__device__ __forceinline__ u64 pack_idx2(int a, int b, u64 epoch) {
+  return ((epoch & 0xFFFFFFFFull) << 32) | ((u64)(unsigned)(a + 1) << 16) | (u64)(unsigned)(b + 1);
+}
+__device__ __forceinline__ bool unpack_idx2(u64 w, u64 epoch, int *a, int *b) {
+  *a = (int)((w >> 16) & 0xFFFFull) - 1;
+  *b = (int)(w & 0xFFFFull) - 1;
+  return (w >> 32) == (epoch & 0xFFFFFFFFull);
+}
+
+__device__ __forceinline__ void spin_pause() { __builtin_amdgcn_s_sleep(2); }
 
 }  // namespace sv

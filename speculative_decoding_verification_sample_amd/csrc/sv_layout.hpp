@@ -7,6 +7,8 @@
 
 namespace sv {
 
+typedef unsigned long long u64;
+
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 
@@ -23,6 +25,16 @@ __host__ __device__ inline int num_splits(int V, int dtype) {
   return (V + split_elems(dtype) - 1) / split_elems(dtype);
 }
 
+// Residual pass geometry: smaller splits (2 vectors per lane) so that the
+// draw for one request is spread over many workgroups.
+constexpr int kVecPerThreadB = 2;
+__host__ __device__ constexpr int split_elems_b(int dtype) {
+  return kThreads * kVecPerThreadB * (16 / elem_bytes(dtype));
+}
+__host__ __device__ inline int num_splits_b(int V, int dtype) {
+  return (V + split_elems_b(dtype) - 1) / split_elems_b(dtype);
+}
+
 // k = log2(e) / T as an unevaluated sum hi + lo of two floats, lo > 0.
 struct Scale {
   float hi, lo;
@@ -36,7 +48,7 @@ struct RowStat {
   float tau;  // smallest kept logit; -inf keeps everything
 };
 
-// Per request, written by the decide kernel for the resample kernels.
+// Per request: the outcome of the ratio tests and what the residual draw needs.
 struct Decision {
   int n;        // accepted drafts (0..K)
   int mode;     // kModeResidual or kModeBonus
@@ -46,18 +58,22 @@ struct Decision {
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
 
-// Per (request, split) partial sums for the inverse-CDF draw.
+// Per (request, residual split) partial sums for the inverse-CDF draw, as
+// self-validating words carrying the call's epoch bits: r = sum of
+// max(0, p' - q') (bonus: p'); p = sum of p' (used if the residual mass is not
+// positive); idx = the split-relative last elements with r > 0 and p' > 0.
 struct ResidPart {
-  double r;    // sum of max(0, p' - q') (bonus: p')
-  double p;    // sum of p' (used if the residual mass is not positive)
-  int last_r;  // last element with r > 0, -1 if none
-  int last_p;  // last element with p' > 0, -1 if none
+  u64 r, p, idx;
 };
+// Largest number of residual splits per row (the draw stages them in LDS).
+constexpr int kMaxSplitsB = 512;
 
 struct Layout {
-  int S = 0;       // splits per row
+  int S = 0;       // streaming splits per row
+  int SB = 0;      // residual splits per row (sampling)
   int rows = 0;    // logit rows streamed
-  size_t part_m = 0, part_z = 0, part_key = 0, rowstat = 0, decision = 0, rpart = 0;
+  size_t part_m = 0, part_z = 0, part_key = 0, part_tag = 0, rowstat = 0, rpart = 0;
+  // sampling: part_m / part_z hold self-validating u64 words per (row, split)
   size_t total = 0;
 };
 
@@ -81,13 +97,14 @@ inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p
     return at;
   };
   if (op == 1) {
-    L.part_m = take(cells * sizeof(float));
-    L.part_z = take(cells * sizeof(double));
+    L.SB = num_splits_b(V, dtype);
+    L.part_m = take(cells * sizeof(u64));
+    L.part_z = take(cells * sizeof(u64));
     L.rowstat = use_top_p ? take((size_t)L.rows * sizeof(RowStat)) : 0;
-    L.decision = take((size_t)B * sizeof(Decision));
-    L.rpart = take((size_t)B * (size_t)L.S * sizeof(ResidPart));
+    L.rpart = take((size_t)B * (size_t)L.SB * sizeof(ResidPart));
   } else {
     L.part_key = take(cells * sizeof(uint64_t));
+    L.part_tag = take(cells * sizeof(u64));
   }
   L.total = off;
   return L;

@@ -1,16 +1,32 @@
-// Sampling verify after the logit rows have been streamed:
-//  - k_sample_decide: one wave64 per request.  Lane i combines the split
-//    partials of target row i and draft row i, evaluates p'(x_i), q'(x_i) in
-//    fp64 and the test u_i * q'(x_i) < p'(x_i); a ballot over the lanes gives
-//    the first rejection n (ariser.io review, section "같은 분포를 지키는 작은
-//    장치": accept with probability min(1, p/q); lotook.com explainer, four
-//    steps: scan left to right, stop at the first mismatch).
-//  - k_resid_partial: per (split, request), the mass of max(0, p'_n - q'_n)
-//    (or p'_K when every draft was accepted: the bonus token) over the split.
-//  - k_sample_locate: per request, the inverse-CDF draw u * S over ascending
-//    token ids: find the split, then the token inside it.
+// Sampling verify in one kernel, k_sample_fused.  Block ids [0, nA) are
+// streaming tiles, one per (request, row, split), requests in order; block
+// ids [nA, nA + nB) are residual tiles, one per (request, residual split).
+// Residual tiles have higher ids than every streaming tile, so they start
+// after all streaming tiles have been dispatched, and they only ever wait for
+// work that is already running (a bounded wait, never forever).  Partials
+// are self-validating words carrying the call's epoch bits, so the workspace
+// needs no clearing between calls, a partial is published with one store and
+// read (and validated) with one load, and no tile performs an atomic
+// read-modify-write.
+//
+// Streaming tile: the split's (max, tempered mass) partial, two words.
+// Residual tile (b, s), once request b's rows are all streamed:
+//  1. decide: combine the (2K+1) x S partials, evaluate p'(x_i), q'(x_i) in
+//     fp64 and the test u_i * q'(x_i) < p'(x_i); a ballot gives the first
+//     rejection n (ariser.io review, section "같은 분포를 지키는 작은 장치":
+//     accept with probability min(1, p/q); lotook.com explainer, four steps:
+//     scan left to right, stop at the first mismatch).  Split 0 writes the
+//     accepted drafts.
+//  2. sum the residual mass max(0, p'_n - q'_n) over the split (p'_K when all
+//     K drafts survived: the bonus token), fp32 terms into fp64, and publish.
+//  3. once every split of the request is published: inverse CDF over
+//     ascending ids, u * S; the tile whose split holds the crossing scans its
+//     register-resident values and one lane walks to the token.
+// With top-p the same kernel runs twice (streaming tiles only, then residual
+// tiles only) around the nucleus kernel, which fills RowStat.
 #include "sv_device.hpp"
 #include "sv_kernels.hpp"
+#include "sv_tiles.hpp"
 
 #pragma clang fp contract(off)
 
@@ -18,330 +34,574 @@ namespace sv {
 
 namespace {
 
-struct RowStatL {
-  float m, tau;
-  double z, zk;
+constexpr int kMaxCells = 1024;  // (2K+1) x S partials combined in LDS
+constexpr int kEntries = kThreads * kVecPerThreadB + 2;
+constexpr int kNoEntry = 0x7FFFFFFF;
+
+// LDS shared by the decide and draw phases of a residual tile.
+struct DecideLds {
+  float cell_m[kMaxCells];
+  double cell_z[kMaxCells];
+  float row_m[128], row_tau[128];
+  double row_zk[128];
+};
+struct DrawLds {
+  double pr[kMaxSplitsB], pp[kMaxSplitsB];
+  int plr[kMaxSplitsB], plp[kMaxSplitsB];
+  double val[kEntries];
+  double tsum[kThreads];
+};
+union TileLds {
+  DecideLds dec;
+  DrawLds draw;
 };
 
-__device__ RowStatL combine_row(const float *part_m, const double *part_z,
-                                const RowStat *rowstat, int row, int S, double k64) {
-  RowStatL r;
-  if (rowstat) {
-    const RowStat rs = rowstat[row];
-    r.m = rs.m;
-    r.tau = rs.tau;
-    r.z = rs.z;
-    r.zk = rs.zk;
-    return r;
-  }
-  const float *pm = part_m + (size_t)row * S;
-  const double *pz = part_z + (size_t)row * S;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, pm[s]);
-  double Z = 0.0;
-  for (int s = 0; s < S; ++s)
-    if (pm[s] > -INFINITY) Z += pz[s] * exp2(((double)pm[s] - (double)M) * k64);
-  r.m = M;
-  r.tau = -INFINITY;
-  r.z = Z;
-  r.zk = Z;
-  return r;
-}
-
 // p'(x) of one row at logit l (fp64): zero outside the nucleus.
-__device__ __forceinline__ double prob_at(float l, const RowStatL &st, double k64) {
-  if (!(l >= st.tau)) return 0.0;
-  return exp2(((double)l - (double)st.m) * k64) / st.zk;
+__device__ __forceinline__ double prob_at(float l, float m, float tau, double zk, double k64) {
+  if (!(l >= tau)) return 0.0;
+  return exp2(((double)l - (double)m) * k64) / zk;
 }
 
-// Residual (or bonus) mass of one token; also its p' for the fallback.
-// Both kernels that scan a row call this, so their per-token values agree.
+// Residual (or bonus) mass of one token, and its p' for the fallback.  Every
+// pass that scans a row calls this, so the per-token values agree bit for bit.
+// Branch-free: for the bonus draw the draft weight inv_d is 0 (and m_d, tau_d
+// repeat the target's), so r = max(p' - 0, 0) = p'.
 __device__ __forceinline__ void resid_terms(float lt, float ld, const Decision &d, Scale k,
                                             double &r, double &p) {
-  double pt = 0.0;
-  if (lt >= d.tau_t) pt = (double)tempered(lt, d.m_t, k) * d.inv_t;
+  const double et = (double)tempered(lt, d.m_t, k) * d.inv_t;
+  const double eq = (double)tempered(ld, d.m_d, k) * d.inv_d;
+  const double pt = lt >= d.tau_t ? et : 0.0;
+  const double qd = ld >= d.tau_d ? eq : 0.0;
+  const double diff = pt - qd;
+  r = diff > 0.0 ? diff : 0.0;
   p = pt;
-  if (d.mode == kModeResidual) {
-    double qd = 0.0;
-    if (ld >= d.tau_d) qd = (double)tempered(ld, d.m_d, k) * d.inv_d;
-    const double diff = pt - qd;
-    r = diff > 0.0 ? diff : 0.0;
-  } else {
-    r = pt;
-  }
 }
 
 __device__ __forceinline__ const char *row_ptr(const void *base, size_t row, int V, int dtype) {
   return (const char *)base + row * (size_t)V * elem_bytes(dtype);
 }
 
-}  // namespace
-
-__global__ __launch_bounds__(64) void k_sample_decide(
-    const char *__restrict__ target, const char *__restrict__ draft, int dtype,
-    const int32_t *__restrict__ tokens, const float *__restrict__ u_accept, int B, int K,
-    int V, int S, double k64, const float *__restrict__ part_m,
-    const double *__restrict__ part_z, const RowStat *__restrict__ rowstat,
-    int32_t *__restrict__ out_accepted, int32_t *__restrict__ out_tokens,
-    float *__restrict__ out_p, float *__restrict__ out_q, Decision *__restrict__ dec) {
-  const int b = blockIdx.x;
-  const int i = threadIdx.x;
-  const int rows_t = B * (K + 1);
-  RowStatL st_t{0.f, 0.f, 1.0, 1.0}, st_d{0.f, 0.f, 1.0, 1.0};
-  if (i <= K) st_t = combine_row(part_m, part_z, rowstat, b * (K + 1) + i, S, k64);
-  if (i < K) st_d = combine_row(part_m, part_z, rowstat, rows_t + b * K + i, S, k64);
-
-  bool accept = false;
-  int x = -1;
-  if (i < K) {
-    x = tokens[(size_t)b * K + i];
-    double p = 0.0, q = 0.0;
-    if (x >= 0 && x < V) {
-      const float lt = load_elem(row_ptr(target, (size_t)b * (K + 1) + i, V, dtype), x, dtype);
-      const float ld = load_elem(row_ptr(draft, (size_t)b * K + i, V, dtype), x, dtype);
-      p = prob_at(lt, st_t, k64);
-      q = prob_at(ld, st_d, k64);
-      const double u = (double)u_accept[(size_t)b * K + i];
-      accept = u * q < p;
-    }
-    if (out_p) out_p[(size_t)b * K + i] = (float)p;
-    if (out_q) out_q[(size_t)b * K + i] = (float)q;
+// One 16-byte group of elements starting at p; assembled from scalar loads
+// when p is not 16-byte aligned.
+template <int DT>
+__device__ __forceinline__ u32x4 load_group(const char *p, bool aligned) {
+  if (aligned) return *reinterpret_cast<const u32x4 *>(p);
+  u32x4 r;
+  if (DT == kBF16) {
+    const uint16_t *h = reinterpret_cast<const uint16_t *>(p);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) r[w] = (uint32_t)h[2 * w] | ((uint32_t)h[2 * w + 1] << 16);
+  } else {
+    const uint32_t *f = reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) r[w] = f[w];
   }
-  const uint64_t acc = __ballot(accept);
-  const uint64_t live = K >= 64 ? ~0ull : ((1ull << K) - 1ull);
-  const uint64_t rej = ~acc & live;
-  const int n = rej ? __builtin_ctzll(rej) : K;
-  if (i <= K) out_tokens[(size_t)b * (K + 1) + i] = i < n ? x : -1;
-  if (i == 0) out_accepted[b] = n;
-  if (i == n) {
-    Decision d;
-    d.n = n;
-    d.mode = n < K ? kModeResidual : kModeBonus;
-    d.m_t = st_t.m;
-    d.tau_t = st_t.tau;
-    d.inv_t = 1.0 / st_t.zk;
-    d.m_d = st_d.m;
-    d.tau_d = st_d.tau;
-    d.inv_d = n < K ? 1.0 / st_d.zk : 0.0;
-    dec[b] = d;
-  }
+  return r;
 }
 
-// Residual partial sums over one split of target row n (and draft row n).
-__global__ __launch_bounds__(kThreads) void k_resid_partial(
-    const char *__restrict__ target, const char *__restrict__ draft, int dtype, int B, int K,
-    int V, int S, Scale k, const Decision *__restrict__ dec, ResidPart *__restrict__ rpart) {
-  const int b = blockIdx.x / S;
-  const int s = blockIdx.x - b * S;
+// Poll one (row, split) cell until it carries this call's epoch.
+__device__ __forceinline__ bool read_cell(const u64 *part_m, const u64 *part_z, size_t g,
+                                          u64 epoch, float *m, double *z) {
+  for (int it = 0; it < kSpinLimit; ++it) {
+    const u64 mw = load_agent(&part_m[g]);
+    const u64 zw = load_agent(&part_z[g]);
+    if (unpack_f32(mw, epoch, m) & unpack_f64(zw, epoch, z)) return true;
+    spin_pause();
+  }
+  return false;
+}
+
+// The accept / reject outcome of request b into *sd; whole workgroup.
+// Returns false if a partial never arrived (bounded wait timed out).
+template <int DT>
+__device__ bool decide(const char *target, const char *draft, const int32_t *tokens,
+                       const float *u_accept, int B, int K, int V, int S, double k64,
+                       const u64 *part_m, const u64 *part_z, u64 epoch,
+                       const RowStat *rowstat, int b, bool write_outputs, int32_t *out_accepted,
+                       int32_t *out_tokens, float *out_p, float *out_q, DecideLds &L,
+                       Decision *sd, int *flag) {
   const int t = threadIdx.x;
-  const Decision d = dec[b];
-  const char *rt = row_ptr(target, (size_t)b * (K + 1) + d.n, V, dtype);
-  const char *rd = d.mode == kModeResidual ? row_ptr(draft, (size_t)b * K + d.n, V, dtype) : rt;
-  const int C = split_elems(dtype);
-  const int e0 = s * C;
-  const int e1 = min(V, e0 + C);
-  const int epv = 16 / elem_bytes(dtype);
-  double sr = 0.0, spp = 0.0;
-  int lr = -1, lp = -1;
-  const Span st = split_span(rt, V, s, dtype);
-  const Span sd = split_span(rd, V, s, dtype);
-  if (st.head == sd.head) {
-    // both rows share the 16-byte phase: vector body plus scalar head/tail
-    const u32x4 *bt = span_body(st, dtype);
-    const u32x4 *bd = span_body(sd, dtype);
-    for (int v = t; v < st.nvec; v += kThreads) {
-      const u32x4 wt = bt[v];
-      const u32x4 wd = bd[v];
-      const int j0 = e0 + st.head + v * epv;
-      for (int e = 0; e < epv; ++e) {
-        double r, p;
-        resid_terms(vec_elem(wt, e, dtype), vec_elem(wd, e, dtype), d, k, r, p);
-        sr += r;
-        spp += p;
-        if (r > 0.0) lr = j0 + e;
-        if (p > 0.0) lp = j0 + e;
-      }
+  const int R = 2 * K + 1;  // local rows: target 0..K, draft K+1..2K
+  const int rows_t = B * (K + 1);
+  auto global_row = [&](int r) {
+    return r <= K ? b * (K + 1) + r : rows_t + b * K + (r - K - 1);
+  };
+  if (t == 0) *flag = 1;
+  // the draft tokens' logits (lanes < K), issued early
+  int x = -1;
+  float lt = 0.f, ld = 0.f;
+  if (t < K) {
+    x = tokens[(size_t)b * K + t];
+    if (x >= 0 && x < V) {
+      lt = load_elem(row_ptr(target, (size_t)b * (K + 1) + t, V, DT), x, DT);
+      ld = load_elem(row_ptr(draft, (size_t)b * K + t, V, DT), x, DT);
     }
-    const int se = span_scalar_elem(st, t, dtype);
-    if (se >= 0) {
-      double r, p;
-      resid_terms(load_elem(rt, e0 + se, dtype), load_elem(rd, e0 + se, dtype), d, k, r, p);
-      sr += r;
-      spp += p;
-      if (r > 0.0) lr = max(lr, e0 + se);
-      if (p > 0.0) lp = max(lp, e0 + se);
-    }
-  } else {
-    for (int j = e0 + t; j < e1; j += kThreads) {
-      double r, p;
-      resid_terms(load_elem(rt, j, dtype), load_elem(rd, j, dtype), d, k, r, p);
-      sr += r;
-      spp += p;
-      if (r > 0.0) lr = j;
-      if (p > 0.0) lp = j;
-    }
-  }
-  // workgroup reduction
-  __shared__ double s_r[kThreads / 64], s_p[kThreads / 64];
-  __shared__ int s_lr[kThreads / 64], s_lp[kThreads / 64];
-  sr = wave_sum(sr);
-  spp = wave_sum(spp);
-  for (int o = 32; o > 0; o >>= 1) {
-    lr = max(lr, __shfl_xor(lr, o, 64));
-    lp = max(lp, __shfl_xor(lp, o, 64));
-  }
-  if (lane_id() == 0) {
-    s_r[t >> 6] = sr;
-    s_p[t >> 6] = spp;
-    s_lr[t >> 6] = lr;
-    s_lp[t >> 6] = lp;
   }
   __syncthreads();
-  if (t == 0) {
-    ResidPart out;
-    out.r = 0.0;
-    out.p = 0.0;
-    out.last_r = -1;
-    out.last_p = -1;
-    for (int w = 0; w < kThreads / 64; ++w) {
-      out.r += s_r[w];
-      out.p += s_p[w];
-      out.last_r = max(out.last_r, s_lr[w]);
-      out.last_p = max(out.last_p, s_lp[w]);
+  if (rowstat) {
+    if (t < R) {
+      const RowStat rs = rowstat[global_row(t)];
+      L.row_m[t] = rs.m;
+      L.row_tau[t] = rs.tau;
+      L.row_zk[t] = rs.zk;
     }
-    rpart[(size_t)b * S + s] = out;
+  } else if (R * S <= kMaxCells) {
+    bool ok = true;
+    for (int c = t; c < R * S; c += kThreads) {
+      float m = -INFINITY;
+      double z = 0.0;
+      ok = ok && read_cell(part_m, part_z, (size_t)global_row(c / S) * S + (c % S), epoch, &m, &z);
+      L.cell_m[c] = m;
+      L.cell_z[c] = z;
+    }
+    if (!ok) *flag = 0;
+    __syncthreads();
+    if (t < R) {
+      float M = -INFINITY;
+      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, L.cell_m[t * S + s2]);
+      L.row_m[t] = M;
+      L.row_tau[t] = -INFINITY;
+    }
+    __syncthreads();
+    for (int c = t; c < R * S; c += kThreads) {
+      const float m = L.cell_m[c], M = L.row_m[c / S];
+      L.cell_z[c] = m > -INFINITY ? L.cell_z[c] * exp2(((double)m - (double)M) * k64) : 0.0;
+    }
+    __syncthreads();
+    if (t < R) {
+      double Z = 0.0;
+      for (int s2 = 0; s2 < S; ++s2) Z += L.cell_z[t * S + s2];
+      L.row_zk[t] = Z;
+    }
+  } else if (t < R) {  // many splits: one lane per row
+    const size_t g0 = (size_t)global_row(t) * S;
+    bool ok = true;
+    float M = -INFINITY;
+    for (int s2 = 0; s2 < S && ok; ++s2) {
+      float m;
+      double z;
+      ok = read_cell(part_m, part_z, g0 + s2, epoch, &m, &z);
+      M = fmaxf(M, m);
+    }
+    double Z = 0.0;
+    for (int s2 = 0; s2 < S && ok; ++s2) {
+      float m;
+      double z;
+      ok = read_cell(part_m, part_z, g0 + s2, epoch, &m, &z);
+      if (m > -INFINITY) Z += z * exp2(((double)m - (double)M) * k64);
+    }
+    if (!ok) *flag = 0;
+    L.row_m[t] = M;
+    L.row_tau[t] = -INFINITY;
+    L.row_zk[t] = Z;
   }
+  __syncthreads();
+  if (t < 64) {
+    const int i = t;
+    bool accept = false;
+    if (i < K) {
+      double p = 0.0, q = 0.0;
+      if (x >= 0 && x < V) {
+        p = prob_at(lt, L.row_m[i], L.row_tau[i], L.row_zk[i], k64);
+        q = prob_at(ld, L.row_m[K + 1 + i], L.row_tau[K + 1 + i], L.row_zk[K + 1 + i], k64);
+        accept = (double)u_accept[(size_t)b * K + i] * q < p;
+      }
+      if (write_outputs && out_p) out_p[(size_t)b * K + i] = (float)p;
+      if (write_outputs && out_q) out_q[(size_t)b * K + i] = (float)q;
+    }
+    const uint64_t acc = __ballot(accept);
+    const uint64_t live = K >= 64 ? ~0ull : ((1ull << K) - 1ull);
+    const uint64_t rej = ~acc & live;
+    const int n = rej ? __builtin_ctzll(rej) : K;
+    if (write_outputs) {
+      if (i <= K && i != n) out_tokens[(size_t)b * (K + 1) + i] = i < n ? x : -1;
+      if (i == 0) out_accepted[b] = n;
+    }
+    if (i == n) {
+      Decision d;
+      d.n = n;
+      d.mode = n < K ? kModeResidual : kModeBonus;
+      d.m_t = L.row_m[n];
+      d.tau_t = L.row_tau[n];
+      d.inv_t = 1.0 / L.row_zk[n];
+      const int dr = n < K ? K + 1 + n : n;  // bonus: the draft terms repeat the target's
+      d.m_d = L.row_m[dr];
+      d.tau_d = L.row_tau[dr];
+      d.inv_d = n < K ? 1.0 / L.row_zk[dr] : 0.0;
+      *sd = d;
+    }
+  }
+  __syncthreads();
+  return *flag != 0;
 }
 
-// Inverse CDF over ascending ids: the smallest j with C_j > u * S.
-__global__ __launch_bounds__(kThreads) void k_sample_locate(
-    const char *__restrict__ target, const char *__restrict__ draft, int dtype,
-    const float *__restrict__ u_sample, int B, int K, int V, int S, Scale k,
-    const Decision *__restrict__ dec, const ResidPart *__restrict__ rpart,
-    int32_t *__restrict__ out_tokens, float *__restrict__ out_mass) {
-  const int b = blockIdx.x;
+template <int DT>
+__device__ void residual_tile(const char *target, const char *draft, const int32_t *tokens,
+                              const float *u_accept, const float *u_sample, int B, int K, int V,
+                              int S, int SB, double k64, Scale k, u64 epoch,
+                              const u64 *part_m, const u64 *part_z, const RowStat *rowstat,
+                              ResidPart *rpart, int32_t *out_accepted, int32_t *out_tokens,
+                              float *out_p, float *out_q, float *out_mass, int b, int s) {
+  constexpr int EPV = 16 / elem_bytes(DT);
+  constexpr int VB = kVecPerThreadB;
   const int t = threadIdx.x;
-  const Decision d = dec[b];
-  const ResidPart *rp = rpart + (size_t)b * S;
-  __shared__ int s_split, s_use_p, s_token;
-  __shared__ double s_rem, s_total;
+  __shared__ TileLds lds;
+  __shared__ Decision sdec;
+  __shared__ int s_ok, s_split, s_use_p, s_fb_split, s_fb_token, s_entry, s_token;
+  __shared__ double s_rem, s_total, s_entry_before;
+
+  // 1. decide, once every streaming tile of request b has published
+  if (!decide<DT>(target, draft, tokens, u_accept, B, K, V, S, k64, part_m, part_z, epoch,
+                  rowstat, b, s == 0, out_accepted, out_tokens, out_p, out_q, lds.dec, &sdec,
+                  &s_ok)) {
+    if (t == 0) out_accepted[b] = -2;  // time-out: flag the request as failed
+    return;
+  }
+  const Decision d = sdec;
+  const char *rt = row_ptr(target, (size_t)b * (K + 1) + d.n, V, DT);
+  const char *rd = d.mode == kModeResidual ? row_ptr(draft, (size_t)b * K + d.n, V, DT) : rt;
+
+  // 2. residual mass over split s, kept in registers per 16-byte group
+  const Span st = split_span_n(rt, V, s, split_elems_b(DT), DT);
+  const Span sq = split_span_n(rd, V, s, split_elems_b(DT), DT);
+  const bool aligned = st.head == sq.head;
+  const int head = aligned ? st.head : 0;
+  const int nvec = aligned ? st.nvec : st.n / EPV;
+  const int tail0 = head + nvec * EPV;
+  const int es = elem_bytes(DT);
+  u32x4 wt[VB], wq[VB];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < VB; ++u) {
+    const int v = t + u * kThreads;
+    const size_t off = (size_t)(head + v * EPV) * es;
+    wt[u] = v < nvec ? load_group<DT>(st.base + off, aligned) : zero;
+    wq[u] = v < nvec ? load_group<DT>(sq.base + off, aligned) : zero;
+  }
+  double cr[VB], cp[VB];
+  int lr = -1, lp = -1;  // split-relative
+#pragma unroll
+  for (int u = 0; u < VB; ++u) {
+    cr[u] = 0.0;
+    cp[u] = 0.0;
+    const int v = t + u * kThreads;
+    if (v < nvec) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        double r, p;
+        resid_terms(vec_elem(wt[u], e, DT), vec_elem(wq[u], e, DT), d, k, r, p);
+        cr[u] += r;
+        cp[u] += p;
+        const int j = head + v * EPV + e;
+        lr = r > 0.0 ? j : lr;
+        lp = p > 0.0 ? j : lp;
+      }
+    }
+  }
+  double hr = 0.0, hp = 0.0, tr = 0.0, tp = 0.0;  // scalar head / tail (lane 0)
+  if (t == 0) {
+    for (int j = 0; j < head; ++j) {
+      double r, p;
+      resid_terms(load_elem(st.base, j, DT), load_elem(sq.base, j, DT), d, k, r, p);
+      hr += r;
+      hp += p;
+      if (r > 0.0) lr = max(lr, j);
+      if (p > 0.0) lp = max(lp, j);
+    }
+    for (int j = tail0; j < st.n; ++j) {
+      double r, p;
+      resid_terms(load_elem(st.base, j, DT), load_elem(sq.base, j, DT), d, k, r, p);
+      tr += r;
+      tp += p;
+      if (r > 0.0) lr = max(lr, j);
+      if (p > 0.0) lp = max(lp, j);
+    }
+  }
+  DrawLds &D = lds.draw;
+  {
+    double own_r = hr + tr, own_p = hp + tp;
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+      own_r += cr[u];
+      own_p += cp[u];
+    }
+    own_r = wave_sum(own_r);
+    own_p = wave_sum(own_p);
+    int wl_r = lr, wl_p = lp;
+    for (int o = 32; o > 0; o >>= 1) {
+      wl_r = max(wl_r, __shfl_xor(wl_r, o, 64));
+      wl_p = max(wl_p, __shfl_xor(wl_p, o, 64));
+    }
+    if (lane_id() == 0) {
+      D.pr[t >> 6] = own_r;
+      D.pp[t >> 6] = own_p;
+      D.plr[t >> 6] = wl_r;
+      D.plp[t >> 6] = wl_p;
+    }
+    __syncthreads();
+    if (t == 0) {
+      double R2 = 0.0, P2 = 0.0;
+      int LR = -1, LP = -1;
+      for (int w = 0; w < kThreads / 64; ++w) {
+        R2 += D.pr[w];
+        P2 += D.pp[w];
+        LR = max(LR, D.plr[w]);
+        LP = max(LP, D.plp[w]);
+      }
+      ResidPart *out = rpart + (size_t)b * SB + s;
+      store_agent(&out->r, pack_f64(R2, epoch));
+      store_agent(&out->p, pack_f64(P2, epoch));
+      store_agent(&out->idx, pack_idx2(LR, LP, epoch));
+    }
+    __syncthreads();  // lane 0 has read the per-wave sums before the LDS is reused
+  }
+
+  // 3. the draw: every residual split of the request has published; which
+  // split holds u * S?
+  DrawLds &D2 = lds.draw;
+  {
+    bool ok = true;
+    const ResidPart *rp = rpart + (size_t)b * SB;
+    for (int i = t; i < SB; i += kThreads) {
+      bool got = false;
+      for (int it = 0; it < kSpinLimit && !got; ++it) {
+        const u64 rw = load_agent(&rp[i].r), pw = load_agent(&rp[i].p), iw = load_agent(&rp[i].idx);
+        double rv, pv;
+        int a, c;
+        got = unpack_f64(rw, epoch, &rv) & unpack_f64(pw, epoch, &pv) & unpack_idx2(iw, epoch, &a, &c);
+        if (got) {
+          D2.pr[i] = rv;
+          D2.pp[i] = pv;
+          D2.plr[i] = a >= 0 ? i * split_elems_b(DT) + a : -1;
+          D2.plp[i] = c >= 0 ? i * split_elems_b(DT) + c : -1;
+        } else {
+          spin_pause();
+        }
+      }
+      ok = ok && got;
+    }
+    if (t == 0) s_ok = 1;
+    __syncthreads();
+    if (!ok) s_ok = 0;
+    __syncthreads();
+    if (!s_ok) {
+      if (t == 0) out_accepted[b] = -2;
+      return;
+    }
+  }
+  auto part_r = [&](int i) { return D2.pr[i]; };
+  auto part_p = [&](int i) { return D2.pp[i]; };
+  auto last_r = [&](int i) { return D2.plr[i]; };
+  auto last_p = [&](int i) { return D2.plp[i]; };
   if (t == 0) {
     double Sr = 0.0;
-    for (int s = 0; s < S; ++s) Sr += rp[s].r;
+    for (int i = 0; i < SB; ++i) Sr += part_r(i);
     int use_p = 0;
     double tot = Sr;
     if (!(Sr > 0.0)) {  // unreachable in exact arithmetic after a rejection
       use_p = 1;
       tot = 0.0;
-      for (int s = 0; s < S; ++s) tot += rp[s].p;
+      for (int i = 0; i < SB; ++i) tot += part_p(i);
     }
-    const double target_mass = (double)u_sample[b] * tot;
+    const double goal = (double)u_sample[b] * tot;
     double c = 0.0;
     int split = -1;
-    for (int s = 0; s < S; ++s) {
-      const double v = use_p ? rp[s].p : rp[s].r;
-      if (c + v > target_mass) {
-        split = s;
+    for (int i = 0; i < SB; ++i) {
+      const double v = use_p ? part_p(i) : part_r(i);
+      if (c + v > goal) {
+        split = i;
         break;
       }
       c += v;
     }
-    int token = -1;
-    if (split < 0) {  // rounding left no crossing: the last token with mass
-      for (int s = S - 1; s >= 0 && token < 0; --s) token = use_p ? rp[s].last_p : rp[s].last_r;
-    }
-    s_split = split;
-    s_use_p = use_p;
-    s_token = token;
-    s_rem = target_mass - c;
-    s_total = tot;
-  }
-  __syncthreads();
-  const int split = s_split;
-  if (split >= 0) {
-    const int use_p = s_use_p;
-    const double rem = s_rem;
-    const char *rt = row_ptr(target, (size_t)b * (K + 1) + d.n, V, dtype);
-    const char *rd = d.mode == kModeResidual ? row_ptr(draft, (size_t)b * K + d.n, V, dtype) : rt;
-    const int C = split_elems(dtype);
-    const int e0 = split * C;
-    const int e1 = min(V, e0 + C);
-    const int per = (e1 - e0 + kThreads - 1) / kThreads;
-    const int j0 = e0 + t * per;
-    const int j1 = min(e1, j0 + per);
-    double own = 0.0;
-    for (int j = j0; j < j1; ++j) {
-      double r, p;
-      resid_terms(load_elem(rt, j, dtype), load_elem(rd, j, dtype), d, k, r, p);
-      own += use_p ? p : r;
-    }
-    // exclusive scan of the per-thread sums (ascending thread = ascending ids)
-    __shared__ double scan[kThreads];
-    scan[t] = own;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const double v = t >= off ? scan[t - off] : 0.0;
-      __syncthreads();
-      scan[t] += v;
-      __syncthreads();
-    }
-    // [scan[t-1], scan[t]) partition [0, scan[last]): at most one thread
-    // holds the crossing and walks its range element by element
-    const double before = t > 0 ? scan[t - 1] : 0.0;
-    if (before <= rem && rem < scan[t] && j0 < j1) {
-      double c = before;
-      int pick = -1, last_pos = -1;
-      for (int j = j0; j < j1; ++j) {
-        double r, p;
-        resid_terms(load_elem(rt, j, dtype), load_elem(rd, j, dtype), d, k, r, p);
-        const double v = use_p ? p : r;
-        if (v > 0.0) last_pos = j;
-        c += v;
-        if (c > rem) {
-          pick = j;
+    int fb_split = 0, fb_token = -1;
+    if (split < 0)  // rounding left no crossing: the last token with mass
+      for (int i = SB - 1; i >= 0; --i) {
+        const int l = use_p ? last_p(i) : last_r(i);
+        if (l >= 0) {
+          fb_split = i;
+          fb_token = l;
           break;
         }
       }
-      s_token = pick >= 0 ? pick : last_pos;
+    s_split = split;
+    s_use_p = use_p;
+    s_rem = goal - c;
+    s_total = tot;
+    s_fb_split = fb_split;
+    s_fb_token = fb_token;
+    s_entry = kNoEntry;
+    s_token = -1;
+  }
+  __syncthreads();
+  const int split = s_split;
+  if (split < 0) {
+    if (s == s_fb_split && t == 0) {
+      out_tokens[(size_t)b * (K + 1) + d.n] = s_fb_token;
+      if (out_mass) out_mass[b] = (float)s_total;
     }
-    __syncthreads();
-    if (t == 0 && s_token < 0) s_token = use_p ? rp[split].last_p : rp[split].last_r;
-    __syncthreads();
+    return;
+  }
+  if (split != s) return;
+
+  // this tile holds the crossing: scan the entries [head | groups | tail]
+  const bool use_p = s_use_p;
+  const double rem = s_rem;
+  const int E = nvec + 2;
+#pragma unroll
+  for (int u = 0; u < VB; ++u) {
+    const int v = t + u * kThreads;
+    if (v < nvec) D.val[1 + v] = use_p ? cp[u] : cr[u];
   }
   if (t == 0) {
-    out_tokens[(size_t)b * (K + 1) + d.n] = s_token;
+    D.val[0] = use_p ? hp : hr;
+    D.val[1 + nvec] = use_p ? tp : tr;
+  }
+  __syncthreads();
+  const int per = (E + kThreads - 1) / kThreads;
+  const int e0 = min(E, t * per), e1 = min(E, e0 + per);
+  double own = 0.0;
+  for (int e = e0; e < e1; ++e) own += D.val[e];
+  D.tsum[t] = own;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const double v = t >= off ? D.tsum[t - off] : 0.0;
+    __syncthreads();
+    D.tsum[t] += v;
+    __syncthreads();
+  }
+  {
+    double c = t > 0 ? D.tsum[t - 1] : 0.0;
+    for (int e = e0; e < e1; ++e) {
+      const double v = D.val[e];
+      if (c <= rem && rem < c + v) atomicMin(&s_entry, e);  // lowest entry wins
+      c += v;
+    }
+  }
+  __syncthreads();
+  const int ent = s_entry;
+  if (ent != kNoEntry && t == 0) {  // the winner's base, summed in the same order
+    const int owner = ent / per;
+    double cc = owner > 0 ? D.tsum[owner - 1] : 0.0;
+    for (int e = owner * per; e < ent; ++e) cc += D.val[e];
+    s_entry_before = cc;
+  }
+  __syncthreads();
+  auto value = [&](float a, float q) {
+    double r, p;
+    resid_terms(a, q, d, k, r, p);
+    return use_p ? p : r;
+  };
+  if (ent != kNoEntry) {
+    const double before = s_entry_before;
+    if (ent == 0 || ent == nvec + 1) {  // the scalar head or tail
+      if (t == 0) {
+        const int j0 = ent == 0 ? 0 : tail0, j1 = ent == 0 ? head : st.n;
+        double cc = before;
+        int pick = -1, last_pos = -1;
+        for (int j = j0; j < j1 && pick < 0; ++j) {
+          const double v = value(load_elem(st.base, j, DT), load_elem(sq.base, j, DT));
+          if (v > 0.0) last_pos = j;
+          cc += v;
+          if (cc > rem) pick = j;
+        }
+        s_token = pick >= 0 ? pick : last_pos;
+      }
+    } else {
+      const int v = ent - 1;
+      if (t == v % kThreads) {
+        const int uu = v / kThreads;
+        u32x4 a = wt[0], q = wq[0];
+#pragma unroll
+        for (int u = 1; u < VB; ++u)
+          if (u == uu) a = wt[u], q = wq[u];
+        double cc = before;
+        int pick = -1, last_pos = -1;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const double val = value(vec_elem(a, e, DT), vec_elem(q, e, DT));
+          const int j = head + v * EPV + e;
+          if (pick < 0) {
+            if (val > 0.0) last_pos = j;
+            cc += val;
+            if (cc > rem) pick = j;
+          }
+        }
+        s_token = pick >= 0 ? pick : last_pos;
+      }
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    int tok = s_token >= 0 ? st.e0 + s_token : -1;
+    if (tok < 0) tok = use_p ? last_p(s) : last_r(s);
+    out_tokens[(size_t)b * (K + 1) + d.n] = tok;
     if (out_mass) out_mass[b] = (float)s_total;
   }
 }
 
-hipError_t launch_sample_decide(const void *target, const void *draft, int dtype,
-                                const int32_t *tokens, const float *u_accept, int B, int K,
-                                int V, int S, double k64, const float *part_m,
-                                const double *part_z, const RowStat *rowstat,
-                                int32_t *out_accepted, int32_t *out_tokens, float *out_p,
-                                float *out_q, Decision *dec, hipStream_t stream) {
-  hipLaunchKernelGGL(k_sample_decide, dim3(B), dim3(64), 0, stream, (const char *)target,
-                     (const char *)draft, dtype, tokens, u_accept, B, K, V, S, k64, part_m,
-                     part_z, rowstat, out_accepted, out_tokens, out_p, out_q, dec);
-  return hipGetLastError();
+}  // namespace
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_sample_fused(
+    const char *__restrict__ target, const char *__restrict__ draft,
+    const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
+    const float *__restrict__ u_sample, int B, int K, int V, int S, int SB, double k64, Scale k,
+    u64 epoch, int block_offset, int nA, u64 *__restrict__ part_m, u64 *__restrict__ part_z,
+    const RowStat *__restrict__ rowstat, ResidPart *__restrict__ rpart,
+    int32_t *__restrict__ out_accepted,
+    int32_t *__restrict__ out_tokens, float *__restrict__ out_p, float *__restrict__ out_q,
+    float *__restrict__ out_mass) {
+  const int blk = (int)blockIdx.x + block_offset;
+  const int R = 2 * K + 1;
+  if (blk < nA) {
+    const int per_req = R * S;
+    const int b = blk / per_req;
+    const int rem = blk - b * per_req;
+    const int r = rem / S;
+    const int s = rem - r * S;
+    const int rows_t = B * (K + 1);
+    const int grow = r <= K ? b * (K + 1) + r : rows_t + b * K + (r - K - 1);
+    const char *rp = r <= K ? row_ptr(target, (size_t)grow, V, DT)
+                            : row_ptr(draft, (size_t)(grow - rows_t), V, DT);
+    float M;
+    double Z;
+    softmax_tile<DT>(rp, V, s, k, &M, &Z);
+    if (threadIdx.x == 0) {
+      store_agent(&part_m[(size_t)grow * S + s], pack_f32(M, epoch));
+      store_agent(&part_z[(size_t)grow * S + s], pack_f64(Z, epoch));
+    }
+    return;
+  }
+  const int cb = blk - nA;
+  const int b = cb / SB;
+  const int s = cb - b * SB;
+  residual_tile<DT>(target, draft, tokens, u_accept, u_sample, B, K, V, S, SB, k64, k, epoch,
+                    part_m, part_z, rowstat, rpart, out_accepted, out_tokens, out_p, out_q,
+                    out_mass, b, s);
 }
 
-hipError_t launch_resid_partial(const void *target, const void *draft, int dtype, int B,
-                                int K, int V, int S, Scale k, const Decision *dec,
-                                ResidPart *rpart, hipStream_t stream) {
-  hipLaunchKernelGGL(k_resid_partial, dim3(S * B), dim3(kThreads), 0, stream,
-                     (const char *)target, (const char *)draft, dtype, B, K, V, S, k, dec,
-                     rpart);
-  return hipGetLastError();
-}
-
-hipError_t launch_sample_locate(const void *target, const void *draft, int dtype,
-                                const float *u_sample, int B, int K, int V, int S, Scale k,
-                                const Decision *dec, const ResidPart *rpart,
-                                int32_t *out_tokens, float *out_mass, hipStream_t stream) {
-  hipLaunchKernelGGL(k_sample_locate, dim3(B), dim3(kThreads), 0, stream,
-                     (const char *)target, (const char *)draft, dtype, u_sample, B, K, V, S,
-                     k, dec, rpart, out_tokens, out_mass);
+hipError_t launch_sample(const void *target, const void *draft, int dtype, const int32_t *tokens,
+                         const float *u_accept, const float *u_sample, int B, int K, int V,
+                         int S, int SB, double k64, Scale k, u64 epoch, int phase,
+                         u64 *part_m, u64 *part_z, const RowStat *rowstat, ResidPart *rpart,
+                         int32_t *out_accepted, int32_t *out_tokens, float *out_p, float *out_q,
+                         float *out_mass, hipStream_t stream) {
+  const int nA = B * (2 * K + 1) * S;
+  const int nB = B * SB;
+  // phase: 0 = both, 1 = streaming tiles only, 2 = residual tiles only
+  const int offset = phase == 2 ? nA : 0;
+  const int blocks = phase == 0 ? nA + nB : phase == 1 ? nA : nB;
+  if (dtype == kBF16)
+    hipLaunchKernelGGL(k_sample_fused<kBF16>, dim3(blocks), dim3(kThreads), 0, stream,
+                       (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
+                       K, V, S, SB, k64, k, epoch, offset, nA, part_m, part_z, rowstat, rpart,
+                       out_accepted, out_tokens, out_p, out_q, out_mass);
+  else
+    hipLaunchKernelGGL(k_sample_fused<kF32>, dim3(blocks), dim3(kThreads), 0, stream,
+                       (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
+                       K, V, S, SB, k64, k, epoch, offset, nA, part_m, part_z, rowstat, rpart,
+                       out_accepted, out_tokens, out_p, out_q, out_mass);
   return hipGetLastError();
 }
 

@@ -1,0 +1,128 @@
+// Streaming tiles: one split of one logit row per 256-lane workgroup, every
+// lane with 8 nontemporal 16-byte loads in flight.  Called by the whole
+// workgroup; the result is valid in thread 0.
+#pragma once
+
+#include "sv_device.hpp"
+
+namespace sv {
+
+template <int DT>
+__device__ __forceinline__ u32x4 neg_inf_vec() {
+  const uint32_t w = DT == kBF16 ? 0xFF80FF80u : 0xFF800000u;
+  u32x4 v = {w, w, w, w};
+  return v;
+}
+
+// Softmax statistics of split s of row `rp`: the maximum M and the tempered
+// mass Z = sum 2^((l - M) k), fp32 terms accumulated in fp64.
+template <int DT>
+__device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale k, float *M_out,
+                                             double *Z_out) {
+  constexpr int EPV = 16 / elem_bytes(DT);
+  const Span sp = split_span(rp, V, s, DT);
+  const u32x4 *body = span_body(sp, DT);
+  const int t = threadIdx.x;
+
+  u32x4 buf[kVecPerThread];
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int v = t + u * kThreads;
+    buf[u] = v < sp.nvec ? load_stream(body + v) : neg_inf_vec<DT>();
+  }
+  const int se = span_scalar_elem(sp, t, DT);
+  const float xs = se >= 0 ? load_elem(sp.base, se, DT) : -INFINITY;
+
+  float m = xs;
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) m = fmaxf(m, vec_elem(buf[u], e, DT));
+
+  double z = 0.0;
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPV; e += 2) {
+        a0 += tempered(vec_elem(buf[u], e, DT), m, k);
+        a1 += tempered(vec_elem(buf[u], e + 1, DT), m, k);
+      }
+      z += (double)(a0 + a1);
+    }
+    if (se >= 0) z += (double)tempered(xs, m, k);
+  }
+
+  // rescale each lane's sum to the wave maximum, then to the workgroup
+  // maximum (factors <= 1, computed from exact differences)
+  __shared__ float sm[kThreads / 64];
+  __shared__ double sz[kThreads / 64];
+  const float wm = wave_max(m);
+  double zz = (m > -INFINITY) ? z * (double)tempered(m, wm, k) : 0.0;
+  zz = wave_sum(zz);
+  if (lane_id() == 0) {
+    sm[t >> 6] = wm;
+    sz[t >> 6] = zz;
+  }
+  __syncthreads();
+  if (t == 0) {
+    float M = sm[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, sm[w]);
+    double Z = 0.0;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w)
+        if (sm[w] > -INFINITY) Z += sz[w] * (double)tempered(sm[w], M, k);
+    }
+    *M_out = M;
+    *Z_out = Z;
+  }
+}
+
+// 64-bit argmax key: order-preserving value key in the high word, the
+// complement of the element index in the low word (ties -> lowest index).
+__device__ __forceinline__ uint64_t argmax_key(float x, uint32_t idx) {
+  return ((uint64_t)key_of_f32(x) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+
+template <int DT>
+__device__ __forceinline__ uint64_t argmax_tile(const char *rp, int V, int s) {
+  constexpr int EPV = 16 / elem_bytes(DT);
+  const Span sp = split_span(rp, V, s, DT);
+  const u32x4 *body = span_body(sp, DT);
+  const int t = threadIdx.x;
+
+  u32x4 buf[kVecPerThread];
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int v = t + u * kThreads;
+    buf[u] = v < sp.nvec ? load_stream(body + v) : neg_inf_vec<DT>();
+  }
+  uint64_t best = 0;
+  const int se = span_scalar_elem(sp, t, DT);
+  if (se >= 0) best = argmax_key(load_elem(sp.base, se, DT), (uint32_t)(sp.e0 + se));
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int v = t + u * kThreads;
+    if (v < sp.nvec) {
+      const uint32_t i0 = (uint32_t)(sp.e0 + sp.head + v * EPV);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const uint64_t key = argmax_key(vec_elem(buf[u], e, DT), i0 + e);
+        best = key > best ? key : best;
+      }
+    }
+  }
+  __shared__ uint64_t sk[kThreads / 64];
+  best = wave_max_u64(best);
+  if (lane_id() == 0) sk[t >> 6] = best;
+  __syncthreads();
+  uint64_t b = sk[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) b = sk[w] > b ? sk[w] : b;
+  return b;
+}
+
+}  // namespace sv

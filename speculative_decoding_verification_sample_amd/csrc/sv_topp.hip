@@ -71,8 +71,8 @@ __device__ __forceinline__ void for_row(const char *row, int V, F &&f) {
 template <int DT>
 __global__ __launch_bounds__(kTopThreads) void k_topp_select(
     const char *__restrict__ target, const char *__restrict__ draft, int rows_t, int V, int S,
-    Scale k, double k64, double top_p, const float *__restrict__ part_m,
-    const double *__restrict__ part_z, RowStat *__restrict__ rowstat) {
+    Scale k, double k64, double top_p, const u64 *__restrict__ part_m,
+    const u64 *__restrict__ part_z, RowStat *__restrict__ rowstat) {
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int w = t >> 6;
@@ -90,14 +90,23 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(
   __shared__ float s_tau;
   __shared__ double s_kept;
 
-  if (t == 0) {
-    const float *pm = part_m + (size_t)row * S;
-    const double *pz = part_z + (size_t)row * S;
+  if (t == 0) {  // the streaming kernel has completed: every partial is in place
+    const u64 *pm = part_m + (size_t)row * S;
+    const u64 *pz = part_z + (size_t)row * S;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pm[s]);
+    for (int s = 0; s < S; ++s) {
+      float m;
+      unpack_f32(pm[s], 0, &m);
+      M = fmaxf(M, m);
+    }
     double Z = 0.0;
-    for (int s = 0; s < S; ++s)
-      if (pm[s] > -INFINITY) Z += pz[s] * exp2(((double)pm[s] - (double)M) * k64);
+    for (int s = 0; s < S; ++s) {
+      float m;
+      double z;
+      unpack_f32(pm[s], 0, &m);
+      unpack_f64(pz[s], 0, &z);
+      if (m > -INFINITY) Z += z * exp2(((double)m - (double)M) * k64);
+    }
     sM = M;
     sZ = Z;
   }
@@ -214,7 +223,7 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(
 
 hipError_t launch_topp_select(const void *target, const void *draft, int dtype, int rows_t,
                               int rows_d, int V, int S, Scale k, double k64, double top_p,
-                              const float *part_m, const double *part_z, RowStat *rowstat,
+                              const u64 *part_m, const u64 *part_z, RowStat *rowstat,
                               hipStream_t stream) {
   dim3 grid(rows_t + rows_d), block(kTopThreads);
   if (dtype == kBF16)
