@@ -169,9 +169,12 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   sv::ResidPart *rpart = carve<sv::ResidPart>(workspace, L.rpart);
   const int rows_t = B * (K + 1), rows_d = B * K;
   const sv::u64 epoch = next_epoch();
+  // residual tiles trail their request's streaming tiles by about one
+  // resident wave of requests
+  const int lag = sv::resident_workgroups(dtype) / ((2 * K + 1) * L.S) + 1;
   auto run = [&](int phase) {
     return sv::launch_sample(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample,
-                             B, K, V, L.S, L.SB, k64, k, epoch, phase, part_m, part_z, rowstat,
+                             B, K, V, L.S, L.SB, k64, k, epoch, phase, lag, part_m, part_z, rowstat,
                              rpart, out_accepted, out_tokens, out_p_draft,
                              out_q_draft, out_residual_mass, stream);
   };

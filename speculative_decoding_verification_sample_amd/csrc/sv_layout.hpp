@@ -25,9 +25,9 @@ __host__ __device__ inline int num_splits(int V, int dtype) {
   return (V + split_elems(dtype) - 1) / split_elems(dtype);
 }
 
-// Residual pass geometry: smaller splits (2 vectors per lane) so that the
-// draw for one request is spread over many workgroups.
-constexpr int kVecPerThreadB = 2;
+// Residual pass geometry: splits of 4 vectors per lane, so that the draw for
+// one request is spread over several workgroups.
+constexpr int kVecPerThreadB = 4;
 __host__ __device__ constexpr int split_elems_b(int dtype) {
   return kThreads * kVecPerThreadB * (16 / elem_bytes(dtype));
 }

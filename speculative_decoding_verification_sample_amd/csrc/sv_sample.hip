@@ -1,9 +1,11 @@
-// Sampling verify in one kernel, k_sample_fused.  Block ids [0, nA) are
-// streaming tiles, one per (request, row, split), requests in order; block
-// ids [nA, nA + nB) are residual tiles, one per (request, residual split).
-// Residual tiles have higher ids than every streaming tile, so they start
-// after all streaming tiles have been dispatched, and they only ever wait for
-// work that is already running (a bounded wait, never forever).  Partials
+// Sampling verify in one kernel, k_sample_fused.  Blocks come in groups
+// g = 0 .. B+L-1: the streaming tiles of request g (one per row split), then
+// the residual tiles of request g - L (one per residual split).  A residual
+// tile is dispatched after every tile it waits for (its request's streaming
+// tiles, L groups earlier, and its sibling residual tiles, adjacent to it),
+// so it only ever waits for work that is already running (a bounded wait,
+// never forever), while the residual work of early requests overlaps the
+// streaming of later ones.  L is about one resident wave of requests.  Partials
 // are self-validating words carrying the call's epoch bits, so the workspace
 // needs no clearing between calls, a partial is published with one store and
 // read (and validated) with one load, and no tile performs an atomic
@@ -24,6 +26,8 @@
 //     register-resident values and one lane walks to the token.
 // With top-p the same kernel runs twice (streaming tiles only, then residual
 // tiles only) around the nucleus kernel, which fills RowStat.
+#include <algorithm>
+
 #include "sv_device.hpp"
 #include "sv_kernels.hpp"
 #include "sv_tiles.hpp"
@@ -235,227 +239,104 @@ __device__ bool decide(const char *target, const char *draft, const int32_t *tok
   return *flag != 0;
 }
 
+// One residual split in registers: the 16-byte groups of target row n and
+// draft row n, their masses per group, and the scalar head / tail (lane 0).
 template <int DT>
-__device__ void residual_tile(const char *target, const char *draft, const int32_t *tokens,
-                              const float *u_accept, const float *u_sample, int B, int K, int V,
-                              int S, int SB, double k64, Scale k, u64 epoch,
-                              const u64 *part_m, const u64 *part_z, const RowStat *rowstat,
-                              ResidPart *rpart, int32_t *out_accepted, int32_t *out_tokens,
-                              float *out_p, float *out_q, float *out_mass, int b, int s) {
+struct SplitRegs {
+  Span st, sq;
+  int head, nvec, tail0;
+  bool aligned;
+  u32x4 wt[kVecPerThreadB], wq[kVecPerThreadB];
+  double cr[kVecPerThreadB], cp[kVecPerThreadB];
+  double hr, hp, tr, tp;
+  int lr, lp;  // split-relative last element with r > 0 / p' > 0 (this lane)
+};
+
+template <int DT>
+__device__ __forceinline__ void load_split(SplitRegs<DT> &X, const char *rt, const char *rd, int V,
+                                           int s, const Decision &d, Scale k) {
   constexpr int EPV = 16 / elem_bytes(DT);
   constexpr int VB = kVecPerThreadB;
   const int t = threadIdx.x;
-  __shared__ TileLds lds;
-  __shared__ Decision sdec;
-  __shared__ int s_ok, s_split, s_use_p, s_fb_split, s_fb_token, s_entry, s_token;
-  __shared__ double s_rem, s_total, s_entry_before;
-
-  // 1. decide, once every streaming tile of request b has published
-  if (!decide<DT>(target, draft, tokens, u_accept, B, K, V, S, k64, part_m, part_z, epoch,
-                  rowstat, b, s == 0, out_accepted, out_tokens, out_p, out_q, lds.dec, &sdec,
-                  &s_ok)) {
-    if (t == 0) out_accepted[b] = -2;  // time-out: flag the request as failed
-    return;
-  }
-  const Decision d = sdec;
-  const char *rt = row_ptr(target, (size_t)b * (K + 1) + d.n, V, DT);
-  const char *rd = d.mode == kModeResidual ? row_ptr(draft, (size_t)b * K + d.n, V, DT) : rt;
-
-  // 2. residual mass over split s, kept in registers per 16-byte group
-  const Span st = split_span_n(rt, V, s, split_elems_b(DT), DT);
-  const Span sq = split_span_n(rd, V, s, split_elems_b(DT), DT);
-  const bool aligned = st.head == sq.head;
-  const int head = aligned ? st.head : 0;
-  const int nvec = aligned ? st.nvec : st.n / EPV;
-  const int tail0 = head + nvec * EPV;
+  X.st = split_span_n(rt, V, s, split_elems_b(DT), DT);
+  X.sq = split_span_n(rd, V, s, split_elems_b(DT), DT);
+  X.aligned = X.st.head == X.sq.head;
+  X.head = X.aligned ? X.st.head : 0;
+  X.nvec = X.aligned ? X.st.nvec : X.st.n / EPV;
+  X.tail0 = X.head + X.nvec * EPV;
   const int es = elem_bytes(DT);
-  u32x4 wt[VB], wq[VB];
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int u = 0; u < VB; ++u) {
     const int v = t + u * kThreads;
-    const size_t off = (size_t)(head + v * EPV) * es;
-    wt[u] = v < nvec ? load_group<DT>(st.base + off, aligned) : zero;
-    wq[u] = v < nvec ? load_group<DT>(sq.base + off, aligned) : zero;
+    const size_t off = (size_t)(X.head + v * EPV) * es;
+    X.wt[u] = v < X.nvec ? load_group<DT>(X.st.base + off, X.aligned) : zero;
+    X.wq[u] = v < X.nvec ? load_group<DT>(X.sq.base + off, X.aligned) : zero;
   }
-  double cr[VB], cp[VB];
-  int lr = -1, lp = -1;  // split-relative
+  X.lr = -1;
+  X.lp = -1;
 #pragma unroll
   for (int u = 0; u < VB; ++u) {
-    cr[u] = 0.0;
-    cp[u] = 0.0;
+    X.cr[u] = 0.0;
+    X.cp[u] = 0.0;
     const int v = t + u * kThreads;
-    if (v < nvec) {
+    if (v < X.nvec) {
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
         double r, p;
-        resid_terms(vec_elem(wt[u], e, DT), vec_elem(wq[u], e, DT), d, k, r, p);
-        cr[u] += r;
-        cp[u] += p;
-        const int j = head + v * EPV + e;
-        lr = r > 0.0 ? j : lr;
-        lp = p > 0.0 ? j : lp;
+        resid_terms(vec_elem(X.wt[u], e, DT), vec_elem(X.wq[u], e, DT), d, k, r, p);
+        X.cr[u] += r;
+        X.cp[u] += p;
+        const int j = X.head + v * EPV + e;
+        X.lr = r > 0.0 ? j : X.lr;
+        X.lp = p > 0.0 ? j : X.lp;
       }
     }
   }
-  double hr = 0.0, hp = 0.0, tr = 0.0, tp = 0.0;  // scalar head / tail (lane 0)
+  X.hr = X.hp = X.tr = X.tp = 0.0;
   if (t == 0) {
-    for (int j = 0; j < head; ++j) {
+    for (int j = 0; j < X.head; ++j) {
       double r, p;
-      resid_terms(load_elem(st.base, j, DT), load_elem(sq.base, j, DT), d, k, r, p);
-      hr += r;
-      hp += p;
-      if (r > 0.0) lr = max(lr, j);
-      if (p > 0.0) lp = max(lp, j);
+      resid_terms(load_elem(X.st.base, j, DT), load_elem(X.sq.base, j, DT), d, k, r, p);
+      X.hr += r;
+      X.hp += p;
+      if (r > 0.0) X.lr = max(X.lr, j);
+      if (p > 0.0) X.lp = max(X.lp, j);
     }
-    for (int j = tail0; j < st.n; ++j) {
+    for (int j = X.tail0; j < X.st.n; ++j) {
       double r, p;
-      resid_terms(load_elem(st.base, j, DT), load_elem(sq.base, j, DT), d, k, r, p);
-      tr += r;
-      tp += p;
-      if (r > 0.0) lr = max(lr, j);
-      if (p > 0.0) lp = max(lp, j);
+      resid_terms(load_elem(X.st.base, j, DT), load_elem(X.sq.base, j, DT), d, k, r, p);
+      X.tr += r;
+      X.tp += p;
+      if (r > 0.0) X.lr = max(X.lr, j);
+      if (p > 0.0) X.lp = max(X.lp, j);
     }
   }
-  DrawLds &D = lds.draw;
-  {
-    double own_r = hr + tr, own_p = hp + tp;
-#pragma unroll
-    for (int u = 0; u < VB; ++u) {
-      own_r += cr[u];
-      own_p += cp[u];
-    }
-    own_r = wave_sum(own_r);
-    own_p = wave_sum(own_p);
-    int wl_r = lr, wl_p = lp;
-    for (int o = 32; o > 0; o >>= 1) {
-      wl_r = max(wl_r, __shfl_xor(wl_r, o, 64));
-      wl_p = max(wl_p, __shfl_xor(wl_p, o, 64));
-    }
-    if (lane_id() == 0) {
-      D.pr[t >> 6] = own_r;
-      D.pp[t >> 6] = own_p;
-      D.plr[t >> 6] = wl_r;
-      D.plp[t >> 6] = wl_p;
-    }
-    __syncthreads();
-    if (t == 0) {
-      double R2 = 0.0, P2 = 0.0;
-      int LR = -1, LP = -1;
-      for (int w = 0; w < kThreads / 64; ++w) {
-        R2 += D.pr[w];
-        P2 += D.pp[w];
-        LR = max(LR, D.plr[w]);
-        LP = max(LP, D.plp[w]);
-      }
-      ResidPart *out = rpart + (size_t)b * SB + s;
-      store_agent(&out->r, pack_f64(R2, epoch));
-      store_agent(&out->p, pack_f64(P2, epoch));
-      store_agent(&out->idx, pack_idx2(LR, LP, epoch));
-    }
-    __syncthreads();  // lane 0 has read the per-wave sums before the LDS is reused
-  }
+}
 
-  // 3. the draw: every residual split of the request has published; which
-  // split holds u * S?
-  DrawLds &D2 = lds.draw;
-  {
-    bool ok = true;
-    const ResidPart *rp = rpart + (size_t)b * SB;
-    for (int i = t; i < SB; i += kThreads) {
-      bool got = false;
-      for (int it = 0; it < kSpinLimit && !got; ++it) {
-        const u64 rw = load_agent(&rp[i].r), pw = load_agent(&rp[i].p), iw = load_agent(&rp[i].idx);
-        double rv, pv;
-        int a, c;
-        got = unpack_f64(rw, epoch, &rv) & unpack_f64(pw, epoch, &pv) & unpack_idx2(iw, epoch, &a, &c);
-        if (got) {
-          D2.pr[i] = rv;
-          D2.pp[i] = pv;
-          D2.plr[i] = a >= 0 ? i * split_elems_b(DT) + a : -1;
-          D2.plp[i] = c >= 0 ? i * split_elems_b(DT) + c : -1;
-        } else {
-          spin_pause();
-        }
-      }
-      ok = ok && got;
-    }
-    if (t == 0) s_ok = 1;
-    __syncthreads();
-    if (!ok) s_ok = 0;
-    __syncthreads();
-    if (!s_ok) {
-      if (t == 0) out_accepted[b] = -2;
-      return;
-    }
-  }
-  auto part_r = [&](int i) { return D2.pr[i]; };
-  auto part_p = [&](int i) { return D2.pp[i]; };
-  auto last_r = [&](int i) { return D2.plr[i]; };
-  auto last_p = [&](int i) { return D2.plp[i]; };
-  if (t == 0) {
-    double Sr = 0.0;
-    for (int i = 0; i < SB; ++i) Sr += part_r(i);
-    int use_p = 0;
-    double tot = Sr;
-    if (!(Sr > 0.0)) {  // unreachable in exact arithmetic after a rejection
-      use_p = 1;
-      tot = 0.0;
-      for (int i = 0; i < SB; ++i) tot += part_p(i);
-    }
-    const double goal = (double)u_sample[b] * tot;
-    double c = 0.0;
-    int split = -1;
-    for (int i = 0; i < SB; ++i) {
-      const double v = use_p ? part_p(i) : part_r(i);
-      if (c + v > goal) {
-        split = i;
-        break;
-      }
-      c += v;
-    }
-    int fb_split = 0, fb_token = -1;
-    if (split < 0)  // rounding left no crossing: the last token with mass
-      for (int i = SB - 1; i >= 0; --i) {
-        const int l = use_p ? last_p(i) : last_r(i);
-        if (l >= 0) {
-          fb_split = i;
-          fb_token = l;
-          break;
-        }
-      }
-    s_split = split;
-    s_use_p = use_p;
-    s_rem = goal - c;
-    s_total = tot;
-    s_fb_split = fb_split;
-    s_fb_token = fb_token;
-    s_entry = kNoEntry;
-    s_token = -1;
-  }
-  __syncthreads();
-  const int split = s_split;
-  if (split < 0) {
-    if (s == s_fb_split && t == 0) {
-      out_tokens[(size_t)b * (K + 1) + d.n] = s_fb_token;
-      if (out_mass) out_mass[b] = (float)s_total;
-    }
-    return;
-  }
-  if (split != s) return;
-
-  // this tile holds the crossing: scan the entries [head | groups | tail]
-  const bool use_p = s_use_p;
-  const double rem = s_rem;
+// Within a split held in registers: the first element whose cumulative mass
+// exceeds `rem` (entries [head | groups | tail] are scanned in id order);
+// split-relative, -1 if rounding left no crossing.  Whole workgroup.
+template <int DT>
+__device__ __forceinline__ int draw_in_split(const SplitRegs<DT> &X, double rem, bool use_p, const Decision &d,
+                             Scale k, DrawLds &D) {
+  constexpr int EPV = 16 / elem_bytes(DT);
+  constexpr int VB = kVecPerThreadB;
+  const int t = threadIdx.x;
+  __shared__ int s_entry, s_token;
+  __shared__ double s_before;
+  const int nvec = X.nvec;
   const int E = nvec + 2;
 #pragma unroll
   for (int u = 0; u < VB; ++u) {
     const int v = t + u * kThreads;
-    if (v < nvec) D.val[1 + v] = use_p ? cp[u] : cr[u];
+    if (v < nvec) D.val[1 + v] = use_p ? X.cp[u] : X.cr[u];
   }
   if (t == 0) {
-    D.val[0] = use_p ? hp : hr;
-    D.val[1 + nvec] = use_p ? tp : tr;
+    D.val[0] = use_p ? X.hp : X.hr;
+    D.val[1 + nvec] = use_p ? X.tp : X.tr;
+    s_entry = kNoEntry;
+    s_token = -1;
   }
   __syncthreads();
   const int per = (E + kThreads - 1) / kThreads;
@@ -484,7 +365,7 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
     const int owner = ent / per;
     double cc = owner > 0 ? D.tsum[owner - 1] : 0.0;
     for (int e = owner * per; e < ent; ++e) cc += D.val[e];
-    s_entry_before = cc;
+    s_before = cc;
   }
   __syncthreads();
   auto value = [&](float a, float q) {
@@ -493,14 +374,14 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
     return use_p ? p : r;
   };
   if (ent != kNoEntry) {
-    const double before = s_entry_before;
+    const double before = s_before;
     if (ent == 0 || ent == nvec + 1) {  // the scalar head or tail
       if (t == 0) {
-        const int j0 = ent == 0 ? 0 : tail0, j1 = ent == 0 ? head : st.n;
+        const int j0 = ent == 0 ? 0 : X.tail0, j1 = ent == 0 ? X.head : X.st.n;
         double cc = before;
         int pick = -1, last_pos = -1;
         for (int j = j0; j < j1 && pick < 0; ++j) {
-          const double v = value(load_elem(st.base, j, DT), load_elem(sq.base, j, DT));
+          const double v = value(load_elem(X.st.base, j, DT), load_elem(X.sq.base, j, DT));
           if (v > 0.0) last_pos = j;
           cc += v;
           if (cc > rem) pick = j;
@@ -511,20 +392,22 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
       const int v = ent - 1;
       if (t == v % kThreads) {
         const int uu = v / kThreads;
-        u32x4 a = wt[0], q = wq[0];
-#pragma unroll
-        for (int u = 1; u < VB; ++u)
-          if (u == uu) a = wt[u], q = wq[u];
         double cc = before;
         int pick = -1, last_pos = -1;
+        // constant register indexes only: the scan is unrolled per group slot
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const double val = value(vec_elem(a, e, DT), vec_elem(q, e, DT));
-          const int j = head + v * EPV + e;
-          if (pick < 0) {
-            if (val > 0.0) last_pos = j;
-            cc += val;
-            if (cc > rem) pick = j;
+        for (int u = 0; u < VB; ++u) {
+          if (u == uu) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+              const double val = value(vec_elem(X.wt[u], e, DT), vec_elem(X.wq[u], e, DT));
+              const int j = X.head + v * EPV + e;
+              if (pick < 0) {
+                if (val > 0.0) last_pos = j;
+                cc += val;
+                if (cc > rem) pick = j;
+              }
+            }
           }
         }
         s_token = pick >= 0 ? pick : last_pos;
@@ -532,9 +415,153 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
     }
   }
   __syncthreads();
+  return s_token;
+}
+
+template <int DT>
+__device__ void residual_tile(const char *target, const char *draft, const int32_t *tokens,
+                              const float *u_accept, const float *u_sample, int B, int K, int V,
+                              int S, int SB, double k64, Scale k, u64 epoch,
+                              const u64 *part_m, const u64 *part_z, const RowStat *rowstat,
+                              ResidPart *rpart, int32_t *out_accepted, int32_t *out_tokens,
+                              float *out_p, float *out_q, float *out_mass, int b, int s) {
+  const int t = threadIdx.x;
+  __shared__ TileLds lds;
+  __shared__ Decision sdec;
+  __shared__ int s_ok, s_split, s_use_p, s_fb_token;
+  __shared__ double s_rem, s_total;
+  __shared__ double red_r[kThreads / 64], red_p[kThreads / 64];
+  __shared__ int red_lr[kThreads / 64], red_lp[kThreads / 64];
+
+  // 1. decide, once every streaming tile of request b has published
+  if (!decide<DT>(target, draft, tokens, u_accept, B, K, V, S, k64, part_m, part_z, epoch,
+                  rowstat, b, s == 0, out_accepted, out_tokens, out_p, out_q, lds.dec, &sdec,
+                  &s_ok)) {
+    if (t == 0) out_accepted[b] = -2;  // time-out: flag the request as failed
+    return;
+  }
+  const Decision d = sdec;
+  const char *rt = row_ptr(target, (size_t)b * (K + 1) + d.n, V, DT);
+  const char *rd = d.mode == kModeResidual ? row_ptr(draft, (size_t)b * K + d.n, V, DT) : rt;
+
+  // 2. the residual mass of split s, published as one record
+  {
+    SplitRegs<DT> X;
+    load_split<DT>(X, rt, rd, V, s, d, k);
+    double own_r = X.hr + X.tr, own_p = X.hp + X.tp;
+#pragma unroll
+    for (int u = 0; u < kVecPerThreadB; ++u) {
+      own_r += X.cr[u];
+      own_p += X.cp[u];
+    }
+    own_r = wave_sum(own_r);
+    own_p = wave_sum(own_p);
+    int wl_r = X.lr, wl_p = X.lp;
+    for (int o = 32; o > 0; o >>= 1) {
+      wl_r = max(wl_r, __shfl_xor(wl_r, o, 64));
+      wl_p = max(wl_p, __shfl_xor(wl_p, o, 64));
+    }
+    if (lane_id() == 0) {
+      red_r[t >> 6] = own_r;
+      red_p[t >> 6] = own_p;
+      red_lr[t >> 6] = wl_r;
+      red_lp[t >> 6] = wl_p;
+    }
+    __syncthreads();
+    if (t == 0) {
+      double R2 = 0.0, P2 = 0.0;
+      int LR = -1, LP = -1;
+      for (int w = 0; w < kThreads / 64; ++w) {
+        R2 += red_r[w];
+        P2 += red_p[w];
+        LR = max(LR, red_lr[w]);
+        LP = max(LP, red_lp[w]);
+      }
+      ResidPart *out = rpart + (size_t)b * SB + s;
+      store_agent(&out->r, pack_f64(R2, epoch));
+      store_agent(&out->p, pack_f64(P2, epoch));
+      store_agent(&out->idx, pack_idx2(LR, LP, epoch));
+    }
+  }
+  // only the request's last residual tile (dispatched after its siblings)
+  // gathers the split masses and draws
+  if (s != SB - 1) return;
+
+  // 3. the draw: which split holds u * S?
+  DrawLds &D = lds.draw;
+  {
+    bool ok = true;
+    const ResidPart *rp = rpart + (size_t)b * SB;
+    for (int i = t; i < SB; i += kThreads) {
+      bool got = false;
+      for (int it = 0; it < kSpinLimit && !got; ++it) {
+        const u64 rw = load_agent(&rp[i].r), pw = load_agent(&rp[i].p), iw = load_agent(&rp[i].idx);
+        double rv, pv;
+        int a, c;
+        got = unpack_f64(rw, epoch, &rv) & unpack_f64(pw, epoch, &pv) & unpack_idx2(iw, epoch, &a, &c);
+        if (got) {
+          D.pr[i] = rv;
+          D.pp[i] = pv;
+          D.plr[i] = a >= 0 ? i * split_elems_b(DT) + a : -1;
+          D.plp[i] = c >= 0 ? i * split_elems_b(DT) + c : -1;
+        } else {
+          spin_pause();
+        }
+      }
+      ok = ok && got;
+    }
+    if (t == 0) s_ok = 1;
+    __syncthreads();
+    if (!ok) s_ok = 0;
+    __syncthreads();
+    if (!s_ok) {
+      if (t == 0) out_accepted[b] = -2;
+      return;
+    }
+  }
   if (t == 0) {
-    int tok = s_token >= 0 ? st.e0 + s_token : -1;
-    if (tok < 0) tok = use_p ? last_p(s) : last_r(s);
+    double Sr = 0.0;
+    for (int i = 0; i < SB; ++i) Sr += D.pr[i];
+    int use_p = 0;
+    double tot = Sr;
+    if (!(Sr > 0.0)) {  // unreachable in exact arithmetic after a rejection
+      use_p = 1;
+      tot = 0.0;
+      for (int i = 0; i < SB; ++i) tot += D.pp[i];
+    }
+    const double goal = (double)u_sample[b] * tot;
+    double c = 0.0;
+    int split = -1;
+    for (int i = 0; i < SB; ++i) {
+      const double v = use_p ? D.pp[i] : D.pr[i];
+      if (c + v > goal) {
+        split = i;
+        break;
+      }
+      c += v;
+    }
+    int fb = -1;  // rounding left no crossing: the last token with mass
+    if (split < 0)
+      for (int i = SB - 1; i >= 0 && fb < 0; --i) fb = use_p ? D.plp[i] : D.plr[i];
+    s_split = split;
+    s_use_p = use_p;
+    s_rem = goal - c;
+    s_total = tot;
+    s_fb_token = split >= 0 ? (use_p ? D.plp[split] : D.plr[split]) : fb;
+  }
+  __syncthreads();
+  const int split = s_split;
+  int tok = s_fb_token;
+  if (split >= 0) {
+    // the crossing split is read again (it is this tile's own split only one
+    // time in SB; keeping that one in registers would cost every tile of the
+    // kernel occupancy)
+    SplitRegs<DT> Y;
+    load_split<DT>(Y, rt, rd, V, split, d, k);
+    const int local = draw_in_split<DT>(Y, s_rem, s_use_p != 0, d, k, D);
+    if (local >= 0) tok = Y.st.e0 + local;
+  }
+  if (t == 0) {
     out_tokens[(size_t)b * (K + 1) + d.n] = tok;
     if (out_mass) out_mass[b] = (float)s_total;
   }
@@ -547,19 +574,39 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     const char *__restrict__ target, const char *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
     const float *__restrict__ u_sample, int B, int K, int V, int S, int SB, double k64, Scale k,
-    u64 epoch, int block_offset, int nA, u64 *__restrict__ part_m, u64 *__restrict__ part_z,
+    u64 epoch, int phase, int lag, u64 *__restrict__ part_m, u64 *__restrict__ part_z,
     const RowStat *__restrict__ rowstat, ResidPart *__restrict__ rpart,
-    int32_t *__restrict__ out_accepted,
-    int32_t *__restrict__ out_tokens, float *__restrict__ out_p, float *__restrict__ out_q,
-    float *__restrict__ out_mass) {
-  const int blk = (int)blockIdx.x + block_offset;
+    int32_t *__restrict__ out_accepted, int32_t *__restrict__ out_tokens,
+    float *__restrict__ out_p, float *__restrict__ out_q, float *__restrict__ out_mass) {
+  const int blk = (int)blockIdx.x;
   const int R = 2 * K + 1;
-  if (blk < nA) {
-    const int per_req = R * S;
-    const int b = blk / per_req;
-    const int rem = blk - b * per_req;
-    const int r = rem / S;
-    const int s = rem - r * S;
+  const int nA_req = R * S;
+  bool streaming;
+  int b, idx;
+  if (phase == 1) {  // streaming tiles only
+    streaming = true;
+    b = blk / nA_req;
+    idx = blk - b * nA_req;
+  } else if (phase == 2) {  // residual tiles only
+    streaming = false;
+    b = blk / SB;
+    idx = blk - b * SB;
+  } else {  // group g holds [streaming(g) | residual(g - lag)]
+    auto prefix = [&](int g) { return nA_req * min(g, B) + SB * min(max(g - lag, 0), B); };
+    int lo = 0, hi = B + lag;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (prefix(mid) <= blk) lo = mid; else hi = mid;
+    }
+    const int off = blk - prefix(lo);
+    const int a_here = lo < B ? nA_req : 0;
+    streaming = off < a_here;
+    b = streaming ? lo : lo - lag;
+    idx = streaming ? off : off - a_here;
+  }
+  if (streaming) {
+    const int r = idx / S;
+    const int s = idx - r * S;
     const int rows_t = B * (K + 1);
     const int grow = r <= K ? b * (K + 1) + r : rows_t + b * K + (r - K - 1);
     const char *rp = r <= K ? row_ptr(target, (size_t)grow, V, DT)
@@ -573,36 +620,50 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     }
     return;
   }
-  const int cb = blk - nA;
-  const int b = cb / SB;
-  const int s = cb - b * SB;
   residual_tile<DT>(target, draft, tokens, u_accept, u_sample, B, K, V, S, SB, k64, k, epoch,
                     part_m, part_z, rowstat, rpart, out_accepted, out_tokens, out_p, out_q,
-                    out_mass, b, s);
+                    out_mass, b, idx);
 }
 
 hipError_t launch_sample(const void *target, const void *draft, int dtype, const int32_t *tokens,
                          const float *u_accept, const float *u_sample, int B, int K, int V,
-                         int S, int SB, double k64, Scale k, u64 epoch, int phase,
+                         int S, int SB, double k64, Scale k, u64 epoch, int phase, int lag,
                          u64 *part_m, u64 *part_z, const RowStat *rowstat, ResidPart *rpart,
                          int32_t *out_accepted, int32_t *out_tokens, float *out_p, float *out_q,
                          float *out_mass, hipStream_t stream) {
   const int nA = B * (2 * K + 1) * S;
   const int nB = B * SB;
-  // phase: 0 = both, 1 = streaming tiles only, 2 = residual tiles only
-  const int offset = phase == 2 ? nA : 0;
+  // phase: 0 = whole call, 1 = streaming tiles only, 2 = residual tiles only
   const int blocks = phase == 0 ? nA + nB : phase == 1 ? nA : nB;
+  lag = std::max(1, std::min(lag, B));
   if (dtype == kBF16)
     hipLaunchKernelGGL(k_sample_fused<kBF16>, dim3(blocks), dim3(kThreads), 0, stream,
                        (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
-                       K, V, S, SB, k64, k, epoch, offset, nA, part_m, part_z, rowstat, rpart,
+                       K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, rowstat, rpart,
                        out_accepted, out_tokens, out_p, out_q, out_mass);
   else
     hipLaunchKernelGGL(k_sample_fused<kF32>, dim3(blocks), dim3(kThreads), 0, stream,
                        (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
-                       K, V, S, SB, k64, k, epoch, offset, nA, part_m, part_z, rowstat, rpart,
+                       K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, rowstat, rpart,
                        out_accepted, out_tokens, out_p, out_q, out_mass);
   return hipGetLastError();
+}
+
+// Workgroups of the fused kernel that fit on the device at once.
+int resident_workgroups(int dtype) {
+  static int cache[2] = {0, 0};
+  const int d = dtype == kBF16 ? 1 : 0;
+  if (!cache[d]) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 2048;
+    const void *fn = d ? (const void *)k_sample_fused<kBF16> : (const void *)k_sample_fused<kF32>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess)
+      per_cu = 4;
+    cache[d] = std::max(1, cus * per_cu);
+  }
+  return cache[d];
 }
 
 }  // namespace sv
