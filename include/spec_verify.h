@@ -44,9 +44,14 @@
  *    device memory and keeps no state between calls (outside the optional
  *    profiling hook below).  Inputs are read-only.
  *  - `workspace` is caller-provided device scratch of at least
- *    spec_verify_workspace_bytes(...) bytes, 256-byte aligned; its contents
- *    are undefined after the call and it must not be shared by calls that
- *    may run concurrently.
+ *    spec_verify_workspace_bytes(...) bytes, 256-byte aligned.  It needs no
+ *    clearing: every call tags what it writes there with fresh epoch bits.
+ *    Its contents are undefined after the call and it must not be shared by
+ *    calls that may run concurrently.
+ *  - Workgroups of one call hand partial results to each other through the
+ *    workspace and wait for them with a bounded spin.  Should such a wait
+ *    ever run out (it waits only on workgroups already dispatched, so it
+ *    should not), the request's out_accepted / out_path_len is set to -2.
  *  - Calls validate every argument on the host first; on any failure they
  *    return a negative SPEC_ERR_* code and enqueue nothing.  On success they
  *    enqueue kernels on `stream` and return SPEC_OK without synchronising;

@@ -21,9 +21,11 @@
 //     accepted drafts.
 //  2. sum the residual mass max(0, p'_n - q'_n) over the split (p'_K when all
 //     K drafts survived: the bonus token), fp32 terms into fp64, and publish.
-//  3. once every split of the request is published: inverse CDF over
-//     ascending ids, u * S; the tile whose split holds the crossing scans its
-//     register-resident values and one lane walks to the token.
+//  3. the request's last residual tile (dispatched after its siblings)
+//     gathers the split masses, finds the split where the cumulative mass
+//     passes u * S (inverse CDF over ascending ids), reads that split again,
+//     scans its per-group masses and one lane walks to the token.  The other
+//     residual tiles exit after publishing.
 // With top-p the same kernel runs twice (streaming tiles only, then residual
 // tiles only) around the nucleus kernel, which fills RowStat.
 #include <algorithm>

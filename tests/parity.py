@@ -5,6 +5,7 @@ import sys
 import numpy as np
 
 import oracle
+import workloads as W
 
 TOL_PROB = 1e-5  # probabilities and residual masses, absolute (fp32 outputs)
 
@@ -101,11 +102,4 @@ def check_tree(w, got, ref):
 
 def subset(w, requests):
     """The same workload restricted to some requests (for oracle sampling)."""
-    import dataclasses
-    r = np.asarray(requests)
-    kw = dict(B=len(r), target=w.target[r])
-    for name in ("draft", "tokens", "u_accept", "u_sample", "parents", "anc_mask"):
-        v = getattr(w, name)
-        if v is not None:
-            kw[name] = v[r]
-    return dataclasses.replace(w, **kw)
+    return W.subset(w, requests)

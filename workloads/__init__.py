@@ -345,3 +345,15 @@ def make_config(index: int, seed: int = 0, B: Optional[int] = None,
         return tree_merged(4, B or 32, n, V or 128256, "bf16", 2.5, 0.6, seed,
                            name=CONFIG_NAMES[4])
     raise ValueError(f"no workload {index}")
+
+
+def subset(w: "Workload", requests) -> "Workload":
+    """The same workload restricted to some of its requests."""
+    import dataclasses
+    r = np.asarray(requests)
+    kw = dict(B=len(r), target=w.target[r])
+    for name in ("draft", "tokens", "u_accept", "u_sample", "parents", "anc_mask"):
+        v = getattr(w, name)
+        if v is not None:
+            kw[name] = v[r]
+    return dataclasses.replace(w, **kw)
