@@ -165,6 +165,7 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   const Scale k = make_scale(k64);
   sv::u64 *part_m = carve<sv::u64>(workspace, L.part_m);
   sv::u64 *part_z = carve<sv::u64>(workspace, L.part_z);
+  sv::u64 *part_x = carve<sv::u64>(workspace, L.part_x);
   sv::RowStat *rowstat = use_top_p ? carve<sv::RowStat>(workspace, L.rowstat) : nullptr;
   sv::ResidPart *rpart = carve<sv::ResidPart>(workspace, L.rpart);
   const int rows_t = B * (K + 1), rows_d = B * K;
@@ -174,7 +175,7 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   const int lag = sv::resident_workgroups(dtype) / ((2 * K + 1) * L.S) + 1;
   auto run = [&](int phase) {
     return sv::launch_sample(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample,
-                             B, K, V, L.S, L.SB, k64, k, epoch, phase, lag, part_m, part_z, rowstat,
+                             B, K, V, L.S, L.SB, k64, k, epoch, phase, lag, part_m, part_z, part_x, rowstat,
                              rpart, out_accepted, out_tokens, out_p_draft,
                              out_q_draft, out_residual_mass, stream);
   };

@@ -241,6 +241,14 @@ __device__ __forceinline__ bool unpack_f64(u64 w, u64 epoch, double *v) {
   *v = __longlong_as_double((long long)(w & ~0xFFFFull));
   return (w & 0xFFFFull) == tag16(epoch);
 }
+// a 32-bit payload in the high word, the epoch's low 32 bits in the low word
+__device__ __forceinline__ u64 pack_u32(uint32_t v, u64 epoch) {
+  return ((u64)v << 32) | (epoch & 0xFFFFFFFFull);
+}
+__device__ __forceinline__ bool unpack_u32(u64 w, u64 epoch, uint32_t *v) {
+  *v = (uint32_t)(w >> 32);
+  return (w & 0xFFFFFFFFull) == (epoch & 0xFFFFFFFFull);
+}
 // two 16-bit indices (each -1 .. 65534) and the epoch's low 32 bits
 __device__ __forceinline__ u64 pack_idx2(int a, int b, u64 epoch) {
   return ((epoch & 0xFFFFFFFFull) << 32) | ((u64)(unsigned)(a + 1) << 16) | (u64)(unsigned)(b + 1);

@@ -119,10 +119,9 @@ __device__ __forceinline__ bool read_cell(const u64 *part_m, const u64 *part_z, 
 
 // The accept / reject outcome of request b into *sd; whole workgroup.
 // Returns false if a partial never arrived (bounded wait timed out).
-template <int DT>
-__device__ bool decide(const char *target, const char *draft, const int32_t *tokens,
-                       const float *u_accept, int B, int K, int V, int S, double k64,
-                       const u64 *part_m, const u64 *part_z, u64 epoch,
+__device__ bool decide(const int32_t *tokens, const float *u_accept, int B, int K, int S,
+                       double k64, const u64 *part_m, const u64 *part_z, const u64 *part_x,
+                       u64 epoch,
                        const RowStat *rowstat, int b, bool write_outputs, int32_t *out_accepted,
                        int32_t *out_tokens, float *out_p, float *out_q, DecideLds &L,
                        Decision *sd, int *flag) {
@@ -133,17 +132,25 @@ __device__ bool decide(const char *target, const char *draft, const int32_t *tok
     return r <= K ? b * (K + 1) + r : rows_t + b * K + (r - K - 1);
   };
   if (t == 0) *flag = 1;
-  // the draft tokens' logits (lanes < K), issued early
+  // the draft tokens (for the emitted prefix) and their logits (lanes < K):
+  // the logits come from the streaming tiles, -inf for a token out of range
   int x = -1;
-  float lt = 0.f, ld = 0.f;
+  float lt = -INFINITY, ld = -INFINITY;
+  bool got_x = true;
   if (t < K) {
     x = tokens[(size_t)b * K + t];
-    if (x >= 0 && x < V) {
-      lt = load_elem(row_ptr(target, (size_t)b * (K + 1) + t, V, DT), x, DT);
-      ld = load_elem(row_ptr(draft, (size_t)b * K + t, V, DT), x, DT);
+    const u64 *px = part_x + ((size_t)b * K + t) * 2;
+    got_x = false;
+    for (int it = 0; it < kSpinLimit && !got_x; ++it) {
+      uint32_t bt, bd;
+      got_x = unpack_u32(load_agent(&px[0]), epoch, &bt) & unpack_u32(load_agent(&px[1]), epoch, &bd);
+      lt = __uint_as_float(bt);
+      ld = __uint_as_float(bd);
+      if (!got_x) spin_pause();
     }
   }
   __syncthreads();
+  if (!got_x) *flag = 0;
   if (rowstat) {
     if (t < R) {
       const RowStat rs = rowstat[global_row(t)];
@@ -206,12 +213,9 @@ __device__ bool decide(const char *target, const char *draft, const int32_t *tok
     const int i = t;
     bool accept = false;
     if (i < K) {
-      double p = 0.0, q = 0.0;
-      if (x >= 0 && x < V) {
-        p = prob_at(lt, L.row_m[i], L.row_tau[i], L.row_zk[i], k64);
-        q = prob_at(ld, L.row_m[K + 1 + i], L.row_tau[K + 1 + i], L.row_zk[K + 1 + i], k64);
-        accept = (double)u_accept[(size_t)b * K + i] * q < p;
-      }
+      const double p = prob_at(lt, L.row_m[i], L.row_tau[i], L.row_zk[i], k64);
+      const double q = prob_at(ld, L.row_m[K + 1 + i], L.row_tau[K + 1 + i], L.row_zk[K + 1 + i], k64);
+      accept = (double)u_accept[(size_t)b * K + i] * q < p;
       if (write_outputs && out_p) out_p[(size_t)b * K + i] = (float)p;
       if (write_outputs && out_q) out_q[(size_t)b * K + i] = (float)q;
     }
@@ -267,13 +271,28 @@ __device__ __forceinline__ void load_split(SplitRegs<DT> &X, const char *rt, con
   X.nvec = X.aligned ? X.st.nvec : X.st.n / EPV;
   X.tail0 = X.head + X.nvec * EPV;
   const int es = elem_bytes(DT);
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // All loads are issued before any is used: lanes past the body re-read its
+  // last group (never used), so no load sits behind a select or a branch.
+  if (X.nvec > 0) {
+    const int last = X.nvec - 1;
+    if (X.aligned) {
+      const u32x4 *bt = reinterpret_cast<const u32x4 *>(X.st.base + (size_t)X.head * es);
+      const u32x4 *bq = reinterpret_cast<const u32x4 *>(X.sq.base + (size_t)X.head * es);
 #pragma unroll
-  for (int u = 0; u < VB; ++u) {
-    const int v = t + u * kThreads;
-    const size_t off = (size_t)(X.head + v * EPV) * es;
-    X.wt[u] = v < X.nvec ? load_group<DT>(X.st.base + off, X.aligned) : zero;
-    X.wq[u] = v < X.nvec ? load_group<DT>(X.sq.base + off, X.aligned) : zero;
+      for (int u = 0; u < VB; ++u) {
+        const int v = min(t + u * kThreads, last);
+        X.wt[u] = bt[v];
+        X.wq[u] = bq[v];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        const int v = min(t + u * kThreads, last);
+        const size_t off = (size_t)(X.head + v * EPV) * es;
+        X.wt[u] = load_group<DT>(X.st.base + off, false);
+        X.wq[u] = load_group<DT>(X.sq.base + off, false);
+      }
+    }
   }
   X.lr = -1;
   X.lp = -1;
@@ -424,9 +443,10 @@ template <int DT>
 __device__ void residual_tile(const char *target, const char *draft, const int32_t *tokens,
                               const float *u_accept, const float *u_sample, int B, int K, int V,
                               int S, int SB, double k64, Scale k, u64 epoch,
-                              const u64 *part_m, const u64 *part_z, const RowStat *rowstat,
-                              ResidPart *rpart, int32_t *out_accepted, int32_t *out_tokens,
-                              float *out_p, float *out_q, float *out_mass, int b, int s) {
+                              const u64 *part_m, const u64 *part_z, const u64 *part_x,
+                              const RowStat *rowstat, ResidPart *rpart, int32_t *out_accepted,
+                              int32_t *out_tokens, float *out_p, float *out_q, float *out_mass,
+                              int b, int s) {
   const int t = threadIdx.x;
   __shared__ TileLds lds;
   __shared__ Decision sdec;
@@ -436,7 +456,7 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
   __shared__ int red_lr[kThreads / 64], red_lp[kThreads / 64];
 
   // 1. decide, once every streaming tile of request b has published
-  if (!decide<DT>(target, draft, tokens, u_accept, B, K, V, S, k64, part_m, part_z, epoch,
+  if (!decide(tokens, u_accept, B, K, S, k64, part_m, part_z, part_x, epoch,
                   rowstat, b, s == 0, out_accepted, out_tokens, out_p, out_q, lds.dec, &sdec,
                   &s_ok)) {
     if (t == 0) out_accepted[b] = -2;  // time-out: flag the request as failed
@@ -577,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
     const float *__restrict__ u_sample, int B, int K, int V, int S, int SB, double k64, Scale k,
     u64 epoch, int phase, int lag, u64 *__restrict__ part_m, u64 *__restrict__ part_z,
-    const RowStat *__restrict__ rowstat, ResidPart *__restrict__ rpart,
+    u64 *__restrict__ part_x, const RowStat *__restrict__ rowstat, ResidPart *__restrict__ rpart,
     int32_t *__restrict__ out_accepted, int32_t *__restrict__ out_tokens,
     float *__restrict__ out_p, float *__restrict__ out_q, float *__restrict__ out_mass) {
   const int blk = (int)blockIdx.x;
@@ -613,26 +633,57 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     const int grow = r <= K ? b * (K + 1) + r : rows_t + b * K + (r - K - 1);
     const char *rp = r <= K ? row_ptr(target, (size_t)grow, V, DT)
                             : row_ptr(draft, (size_t)(grow - rows_t), V, DT);
+    // the draft token's logit, if this split holds it (or, for a token out
+    // of range, split 0 publishes -inf: probability 0, the draft is rejected)
+    // (uniform across the workgroup: scalar registers, no vector registers
+    // held across the stream)
+    const int pos = r <= K ? r : r - K - 1;  // position; target row K has no draft token
+    bool mine = false, valid = false;
+    unsigned mis = 0;
+    uint32_t w = 0;
+    if (r != K) {
+      const int x = tokens[(size_t)b * K + pos];
+      const int e0 = s * split_elems(DT), e1 = min(V, e0 + split_elems(DT));
+      valid = x >= 0 && x < V;
+      mine = (valid && x >= e0 && x < e1) || (!valid && s == 0);
+      if (mine && valid) {
+        // the aligned dword holding the element (same page, so always
+        // readable); its bits are picked apart only after the stream
+        // the logits are read-only for the whole call: a scalar load through
+        // the constant address space, which leaves the vector queue to the
+        // stream
+        typedef const __attribute__((address_space(4))) uint32_t *const_u32p;
+        const uintptr_t ea = reinterpret_cast<uintptr_t>(rp) + (uintptr_t)x * elem_bytes(DT);
+        mis = (unsigned)(ea & 3u);
+        w = *(const_u32p)(ea - mis);
+      }
+    }
     float M;
     double Z;
     softmax_tile<DT>(rp, V, s, k, &M, &Z);
     if (threadIdx.x == 0) {
       store_agent(&part_m[(size_t)grow * S + s], pack_f32(M, epoch));
       store_agent(&part_z[(size_t)grow * S + s], pack_f64(Z, epoch));
+      if (mine) {
+        const uint32_t lx_bits = !valid ? 0xFF800000u  // -inf
+                                 : DT == kBF16 ? (mis ? (w & 0xFFFF0000u) : (w << 16)) : w;
+        store_agent(part_x + ((size_t)b * K + pos) * 2 + (r <= K ? 0 : 1),
+                    pack_u32(lx_bits, epoch));
+      }
     }
     return;
   }
   residual_tile<DT>(target, draft, tokens, u_accept, u_sample, B, K, V, S, SB, k64, k, epoch,
-                    part_m, part_z, rowstat, rpart, out_accepted, out_tokens, out_p, out_q,
-                    out_mass, b, idx);
+                    part_m, part_z, part_x, rowstat, rpart, out_accepted, out_tokens, out_p,
+                    out_q, out_mass, b, idx);
 }
 
 hipError_t launch_sample(const void *target, const void *draft, int dtype, const int32_t *tokens,
                          const float *u_accept, const float *u_sample, int B, int K, int V,
                          int S, int SB, double k64, Scale k, u64 epoch, int phase, int lag,
-                         u64 *part_m, u64 *part_z, const RowStat *rowstat, ResidPart *rpart,
-                         int32_t *out_accepted, int32_t *out_tokens, float *out_p, float *out_q,
-                         float *out_mass, hipStream_t stream) {
+                         u64 *part_m, u64 *part_z, u64 *part_x, const RowStat *rowstat,
+                         ResidPart *rpart, int32_t *out_accepted, int32_t *out_tokens,
+                         float *out_p, float *out_q, float *out_mass, hipStream_t stream) {
   const int nA = B * (2 * K + 1) * S;
   const int nB = B * SB;
   // phase: 0 = whole call, 1 = streaming tiles only, 2 = residual tiles only
@@ -641,13 +692,13 @@ hipError_t launch_sample(const void *target, const void *draft, int dtype, const
   if (dtype == kBF16)
     hipLaunchKernelGGL(k_sample_fused<kBF16>, dim3(blocks), dim3(kThreads), 0, stream,
                        (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
-                       K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, rowstat, rpart,
-                       out_accepted, out_tokens, out_p, out_q, out_mass);
+                       K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, part_x, rowstat,
+                       rpart, out_accepted, out_tokens, out_p, out_q, out_mass);
   else
     hipLaunchKernelGGL(k_sample_fused<kF32>, dim3(blocks), dim3(kThreads), 0, stream,
                        (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
-                       K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, rowstat, rpart,
-                       out_accepted, out_tokens, out_p, out_q, out_mass);
+                       K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, part_x, rowstat,
+                       rpart, out_accepted, out_tokens, out_p, out_q, out_mass);
   return hipGetLastError();
 }
 
