@@ -39,19 +39,33 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
 #pragma unroll
     for (int e = 0; e < EPV; ++e) m = fmaxf(m, vec_elem(buf[u], e, DT));
 
+  // 2^((l - m) k) with k = hi + lo: the exponent is taken as
+  // (l hi + c) + l lo with c = -m hi rounded to a float (two fused
+  // multiply-adds, each product exact); the parts left out, the rounding
+  // e = -m hi - c (exact by one more fused multiply-add) and -m lo, are
+  // the same for every element and scale the lane's sum once, in fp64.
   double z = 0.0;
   if (m > -INFINITY) {
+    const float c = -m * k.hi;
+    const float e = fmaf(-m, k.hi, -c);
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
-      float a0 = 0.f, a1 = 0.f;
+      auto term = [&](int j) {
+        const float x = vec_elem(buf[u], j, DT);
+        return exp2_fast(fmaf(x, k.lo, fmaf(x, k.hi, c)));
+      };
+      float a0 = term(0), a1 = term(1);
 #pragma unroll
-      for (int e = 0; e < EPV; e += 2) {
-        a0 += tempered(vec_elem(buf[u], e, DT), m, k);
-        a1 += tempered(vec_elem(buf[u], e + 1, DT), m, k);
+      for (int j = 2; j < EPV; j += 2) {
+        a0 += term(j);
+        a1 += term(j + 1);
       }
       z += (double)(a0 + a1);
     }
-    if (se >= 0) z += (double)tempered(xs, m, k);
+    if (se >= 0) z += (double)exp2_fast(fmaf(xs, k.lo, fmaf(xs, k.hi, c)));
+    // 2^delta for |delta| < 1e-5: 1 + delta ln2 + (delta ln2)^2 / 2, error < 1e-16
+    const double dl = ((double)e - (double)m * (double)k.lo) * 0.6931471805599453;
+    z *= 1.0 + dl * (1.0 + 0.5 * dl);
   }
 
   // rescale each lane's sum to the wave maximum, then to the workgroup
