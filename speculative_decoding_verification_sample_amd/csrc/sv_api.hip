@@ -167,7 +167,8 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   sv::u64 *part_z = carve<sv::u64>(workspace, L.part_z);
   sv::u64 *part_x = carve<sv::u64>(workspace, L.part_x);
   sv::RowStat *rowstat = use_top_p ? carve<sv::RowStat>(workspace, L.rowstat) : nullptr;
-  sv::ResidPart *rpart = carve<sv::ResidPart>(workspace, L.rpart);
+  sv::u64 *rtot = carve<sv::u64>(workspace, L.rtot);
+  sv::u64 *rent = carve<sv::u64>(workspace, L.rent);
   const int rows_t = B * (K + 1), rows_d = B * K;
   const sv::u64 epoch = next_epoch();
   // residual tiles trail their request's streaming tiles by about one
@@ -176,7 +177,7 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   auto run = [&](int phase) {
     return sv::launch_sample(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample,
                              B, K, V, L.S, L.SB, k64, k, epoch, phase, lag, part_m, part_z, part_x, rowstat,
-                             rpart, out_accepted, out_tokens, out_p_draft,
+                             rtot, rent, out_accepted, out_tokens, out_p_draft,
                              out_q_draft, out_residual_mass, stream);
   };
   prof_before(stream);

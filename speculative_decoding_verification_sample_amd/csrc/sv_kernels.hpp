@@ -23,7 +23,7 @@ hipError_t launch_sample(const void *target, const void *draft, int dtype, const
                          const float *u_accept, const float *u_sample, int B, int K, int V,
                          int S, int SB, double k64, Scale k, u64 epoch, int phase, int lag,
                          u64 *part_m, u64 *part_z, u64 *part_x, const RowStat *rowstat,
-                         ResidPart *rpart, int32_t *out_accepted,
+                         u64 *rtot, u64 *rent, int32_t *out_accepted,
                          int32_t *out_tokens, float *out_p, float *out_q, float *out_mass,
                          hipStream_t stream);
 

@@ -48,23 +48,26 @@ struct RowStat {
   float tau;  // smallest kept logit; -inf keeps everything
 };
 
-// Per request: the outcome of the ratio tests and what the residual draw needs.
+// Per request: the outcome of the ratio tests and what the residual draw
+// needs.  A token's mass in row n is 2^((l - m) k) / kept mass, with the
+// difference l - m exact, so that equal rows give equal masses bit for bit
+// and a row's maximum weighs exactly 1 / kept mass.
 struct Decision {
-  int n;        // accepted drafts (0..K)
-  int mode;     // kModeResidual or kModeBonus
-  float m_t, tau_t, m_d, tau_d;
-  double inv_t, inv_d;  // 1 / kept mass of target row n / draft row n
+  int n;                // accepted drafts (0..K)
+  int mode;             // kModeResidual or kModeBonus
+  float m_t, m_d;       // maxima of target row n / draft row n
+  float tau_t, tau_d;   // smallest kept logits (-inf: all kept)
+  double inv_t, inv_d;  // 1 / kept mass; inv_d = 0 for the bonus draw (r = p')
 };
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
 
-// Per (request, residual split) partial sums for the inverse-CDF draw, as
-// self-validating words carrying the call's epoch bits: r = sum of
-// max(0, p' - q') (bonus: p'); p = sum of p' (used if the residual mass is not
-// positive); idx = the split-relative last elements with r > 0 and p' > 0.
-struct ResidPart {
-  u64 r, p, idx;
-};
+// Residual draw records, self-validating words carrying the call's epoch
+// bits: per (request, residual split) the split's mass, and per entry of the
+// split the entry's mass.  Entries: 0 = the scalar head of the split, 1 + t =
+// the body groups of lane t (kVecPerThreadB consecutive groups), kThreads + 1
+// = the scalar tail; in that order they follow ascending token ids.
+constexpr int kEntriesB = kThreads + 2;
 // Largest number of residual splits per row (the draw stages them in LDS).
 constexpr int kMaxSplitsB = 512;
 
@@ -72,7 +75,8 @@ struct Layout {
   int S = 0;       // streaming splits per row
   int SB = 0;      // residual splits per row (sampling)
   int rows = 0;    // logit rows streamed
-  size_t part_m = 0, part_z = 0, part_x = 0, part_key = 0, part_tag = 0, rowstat = 0, rpart = 0;
+  size_t part_m = 0, part_z = 0, part_x = 0, part_key = 0, part_tag = 0, rowstat = 0;
+  size_t rtot = 0, rent = 0;
   // sampling: part_m / part_z hold self-validating u64 words per (row, split);
   // part_x one word per (request, position, target / draft): the logit of the
   // draft token, written by the streaming tile whose split holds it
@@ -104,7 +108,8 @@ inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p
     L.part_z = take(cells * sizeof(u64));
     L.part_x = take((size_t)B * (size_t)KN * 2 * sizeof(u64));
     L.rowstat = use_top_p ? take((size_t)L.rows * sizeof(RowStat)) : 0;
-    L.rpart = take((size_t)B * (size_t)L.SB * sizeof(ResidPart));
+    L.rtot = take((size_t)B * (size_t)L.SB * sizeof(u64));
+    L.rent = take((size_t)B * (size_t)L.SB * kEntriesB * sizeof(u64));
   } else {
     L.part_key = take(cells * sizeof(uint64_t));
     L.part_tag = take(cells * sizeof(u64));

@@ -41,8 +41,6 @@ namespace sv {
 namespace {
 
 constexpr int kMaxCells = 1024;  // (2K+1) x S partials combined in LDS
-constexpr int kEntries = kThreads * kVecPerThreadB + 2;
-constexpr int kNoEntry = 0x7FFFFFFF;
 
 // LDS shared by the decide and draw phases of a residual tile.
 struct DecideLds {
@@ -52,14 +50,21 @@ struct DecideLds {
   double row_zk[128];
 };
 struct DrawLds {
-  double pr[kMaxSplitsB], pp[kMaxSplitsB];
-  int plr[kMaxSplitsB], plp[kMaxSplitsB];
-  double val[kEntries];
-  double tsum[kThreads];
+  double tot[kMaxSplitsB];  // split masses of the request
+  double wsum[kThreads / 64], wprev[kThreads / 64], lanes_end;
+  int wfirst[kThreads / 64], wlast[kThreads / 64];
 };
 union TileLds {
   DecideLds dec;
   DrawLds draw;
+};
+// Everything a residual tile keeps in LDS (one allocation for the kernel).
+struct ResidLds {
+  TileLds lds;
+  Decision dec;
+  int ok, split, use_p;
+  double rem, total;
+  double red[kThreads / 64];
 };
 
 // p'(x) of one row at logit l (fp64): zero outside the nucleus.
@@ -68,19 +73,18 @@ __device__ __forceinline__ double prob_at(float l, float m, float tau, double zk
   return exp2(((double)l - (double)m) * k64) / zk;
 }
 
-// Residual (or bonus) mass of one token, and its p' for the fallback.  Every
-// pass that scans a row calls this, so the per-token values agree bit for bit.
-// Branch-free: for the bonus draw the draft weight inv_d is 0 (and m_d, tau_d
-// repeat the target's), so r = max(p' - 0, 0) = p'.
-__device__ __forceinline__ void resid_terms(float lt, float ld, const Decision &d, Scale k,
-                                            double &r, double &p) {
-  const double et = (double)tempered(lt, d.m_t, k) * d.inv_t;
-  const double eq = (double)tempered(ld, d.m_d, k) * d.inv_d;
-  const double pt = lt >= d.tau_t ? et : 0.0;
-  const double qd = ld >= d.tau_d ? eq : 0.0;
-  const double diff = pt - qd;
-  r = diff > 0.0 ? diff : 0.0;
-  p = pt;
+// Mass of one token of the drawn row pair: the residual r = max(0, p' - q')
+// (the bonus draw has w_d = 0, so r = p'), or p' itself (P: the fallback when
+// the residual mass is not positive).  Every pass over the pair computes it
+// with this one function, so the values agree bit for bit.
+template <bool TOPP, bool P>
+__device__ __forceinline__ double token_mass(float lt, float ld, const Decision &d, Scale k) {
+  double pt = (double)tempered(lt, d.m_t, k) * d.inv_t;
+  if (TOPP) pt = lt >= d.tau_t ? pt : 0.0;
+  if (P) return pt;
+  double qd = (double)tempered(ld, d.m_d, k) * d.inv_d;
+  if (TOPP) qd = ld >= d.tau_d ? qd : 0.0;
+  return fmax(pt - qd, 0.0);
 }
 
 __device__ __forceinline__ const char *row_ptr(const void *base, size_t row, int V, int dtype) {
@@ -120,8 +124,8 @@ __device__ __forceinline__ bool read_cell(const u64 *part_m, const u64 *part_z, 
 // The accept / reject outcome of request b into *sd; whole workgroup.
 // Returns false if a partial never arrived (bounded wait timed out).
 __device__ bool decide(const int32_t *tokens, const float *u_accept, int B, int K, int S,
-                       double k64, const u64 *part_m, const u64 *part_z, const u64 *part_x,
-                       u64 epoch,
+                       double k64, Scale k, const u64 *part_m, const u64 *part_z,
+                       const u64 *part_x, u64 epoch,
                        const RowStat *rowstat, int b, bool write_outputs, int32_t *out_accepted,
                        int32_t *out_tokens, float *out_p, float *out_q, DecideLds &L,
                        Decision *sd, int *flag) {
@@ -234,10 +238,15 @@ __device__ bool decide(const int32_t *tokens, const float *u_accept, int B, int 
       d.m_t = L.row_m[n];
       d.tau_t = L.row_tau[n];
       d.inv_t = 1.0 / L.row_zk[n];
-      const int dr = n < K ? K + 1 + n : n;  // bonus: the draft terms repeat the target's
-      d.m_d = L.row_m[dr];
-      d.tau_d = L.row_tau[dr];
-      d.inv_d = n < K ? 1.0 / L.row_zk[dr] : 0.0;
+      if (n < K) {
+        d.m_d = L.row_m[K + 1 + n];
+        d.tau_d = L.row_tau[K + 1 + n];
+        d.inv_d = 1.0 / L.row_zk[K + 1 + n];
+      } else {  // bonus: no draft row; its weight 0 makes the residual p'
+        d.m_d = d.m_t;
+        d.tau_d = d.tau_t;
+        d.inv_d = 0.0;
+      }
       *sd = d;
     }
   }
@@ -245,220 +254,219 @@ __device__ bool decide(const int32_t *tokens, const float *u_accept, int B, int 
   return *flag != 0;
 }
 
-// One residual split in registers: the 16-byte groups of target row n and
-// draft row n, their masses per group, and the scalar head / tail (lane 0).
-template <int DT>
-struct SplitRegs {
-  Span st, sq;
-  int head, nvec, tail0;
-  bool aligned;
-  u32x4 wt[kVecPerThreadB], wq[kVecPerThreadB];
-  double cr[kVecPerThreadB], cp[kVecPerThreadB];
-  double hr, hp, tr, tp;
-  int lr, lp;  // split-relative last element with r > 0 / p' > 0 (this lane)
+// ---------------------------------------------------------------------------
+// residual (or bonus) draw
+// ---------------------------------------------------------------------------
+
+// One residual split of the drawn row pair.  Lane t owns body groups
+// [t VB, t VB + VB) (consecutive, so a lane's entry is a run of token ids).
+struct SplitGeo {
+  const char *bt, *bq;  // element 0 of the split in the target / draft row
+  int e0, n;            // first element (row-relative) and elements in the split
+  int head, nvec, tail0;  // scalar head, 16-byte groups, first tail element
+  bool aligned;           // both rows share the 16-byte phase: vector loads
 };
 
 template <int DT>
-__device__ __forceinline__ void load_split(SplitRegs<DT> &X, const char *rt, const char *rd, int V,
-                                           int s, const Decision &d, Scale k) {
+__device__ __forceinline__ SplitGeo split_geo(const char *rt, const char *rd, int V, int s) {
+  constexpr int EPV = 16 / elem_bytes(DT);
+  const Span a = split_span_n(rt, V, s, split_elems_b(DT), DT);
+  const Span q = split_span_n(rd, V, s, split_elems_b(DT), DT);
+  SplitGeo g;
+  g.bt = a.base;
+  g.bq = q.base;
+  g.e0 = a.e0;
+  g.n = a.n;
+  g.aligned = a.head == q.head;
+  g.head = g.aligned ? a.head : 0;  // misaligned pair: groups assembled from scalars
+  g.nvec = g.aligned ? a.nvec : a.n / EPV;
+  g.tail0 = g.head + g.nvec * EPV;
+  return g;
+}
+
+// Split-relative element range [j0, j1) of entry `ent`.
+template <int DT>
+__device__ __forceinline__ void entry_range(const SplitGeo &g, int ent, int &j0, int &j1) {
   constexpr int EPV = 16 / elem_bytes(DT);
   constexpr int VB = kVecPerThreadB;
-  const int t = threadIdx.x;
-  X.st = split_span_n(rt, V, s, split_elems_b(DT), DT);
-  X.sq = split_span_n(rd, V, s, split_elems_b(DT), DT);
-  X.aligned = X.st.head == X.sq.head;
-  X.head = X.aligned ? X.st.head : 0;
-  X.nvec = X.aligned ? X.st.nvec : X.st.n / EPV;
-  X.tail0 = X.head + X.nvec * EPV;
-  const int es = elem_bytes(DT);
-  // All loads are issued before any is used: lanes past the body re-read its
-  // last group (never used), so no load sits behind a select or a branch.
-  if (X.nvec > 0) {
-    const int last = X.nvec - 1;
-    if (X.aligned) {
-      const u32x4 *bt = reinterpret_cast<const u32x4 *>(X.st.base + (size_t)X.head * es);
-      const u32x4 *bq = reinterpret_cast<const u32x4 *>(X.sq.base + (size_t)X.head * es);
+  if (ent == 0) {
+    j0 = 0;
+    j1 = g.head;
+  } else if (ent == kThreads + 1) {
+    j0 = g.tail0;
+    j1 = g.n;
+  } else {
+    j0 = g.head + min((ent - 1) * VB, g.nvec) * EPV;
+    j1 = g.head + min(ent * VB, g.nvec) * EPV;
+  }
+}
+
+// Mass of this lane's body entry.  All loads are issued before any is used;
+// lanes past the body re-read its last group (never used).
+template <int DT, bool TOPP, bool P>
+__device__ __forceinline__ double lane_mass(const SplitGeo &g, const Decision &d, Scale k) {
+  constexpr int EPV = 16 / elem_bytes(DT);
+  constexpr int VB = kVecPerThreadB;
+  const int v0 = threadIdx.x * VB;
+  double acc = 0.0;
+  if (g.nvec > 0) {
+    const int last = g.nvec - 1;
+    const int es = elem_bytes(DT);
+    u32x4 wt[VB], wq[VB];
+    if (g.aligned) {
+      const u32x4 *pt = reinterpret_cast<const u32x4 *>(g.bt + (size_t)g.head * es);
+      const u32x4 *pq = reinterpret_cast<const u32x4 *>(g.bq + (size_t)g.head * es);
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
-        const int v = min(t + u * kThreads, last);
-        X.wt[u] = bt[v];
-        X.wq[u] = bq[v];
+        const int v = min(v0 + u, last);
+        wt[u] = pt[v];
+        if (!P) wq[u] = pq[v];
       }
     } else {
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
-        const int v = min(t + u * kThreads, last);
-        const size_t off = (size_t)(X.head + v * EPV) * es;
-        X.wt[u] = load_group<DT>(X.st.base + off, false);
-        X.wq[u] = load_group<DT>(X.sq.base + off, false);
+        const size_t off = (size_t)min(v0 + u, last) * EPV * es;
+        wt[u] = load_group<DT>(g.bt + off, false);
+        if (!P) wq[u] = load_group<DT>(g.bq + off, false);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+      if (v0 + u < g.nvec) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+          acc += token_mass<TOPP, P>(vec_elem(wt[u], e, DT), P ? 0.f : vec_elem(wq[u], e, DT), d, k);
       }
     }
   }
-  X.lr = -1;
-  X.lp = -1;
-#pragma unroll
-  for (int u = 0; u < VB; ++u) {
-    X.cr[u] = 0.0;
-    X.cp[u] = 0.0;
-    const int v = t + u * kThreads;
-    if (v < X.nvec) {
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        double r, p;
-        resid_terms(vec_elem(X.wt[u], e, DT), vec_elem(X.wq[u], e, DT), d, k, r, p);
-        X.cr[u] += r;
-        X.cp[u] += p;
-        const int j = X.head + v * EPV + e;
-        X.lr = r > 0.0 ? j : X.lr;
-        X.lp = p > 0.0 ? j : X.lp;
-      }
-    }
-  }
-  X.hr = X.hp = X.tr = X.tp = 0.0;
-  if (t == 0) {
-    for (int j = 0; j < X.head; ++j) {
-      double r, p;
-      resid_terms(load_elem(X.st.base, j, DT), load_elem(X.sq.base, j, DT), d, k, r, p);
-      X.hr += r;
-      X.hp += p;
-      if (r > 0.0) X.lr = max(X.lr, j);
-      if (p > 0.0) X.lp = max(X.lp, j);
-    }
-    for (int j = X.tail0; j < X.st.n; ++j) {
-      double r, p;
-      resid_terms(load_elem(X.st.base, j, DT), load_elem(X.sq.base, j, DT), d, k, r, p);
-      X.tr += r;
-      X.tp += p;
-      if (r > 0.0) X.lr = max(X.lr, j);
-      if (p > 0.0) X.lp = max(X.lp, j);
-    }
-  }
+  return acc;
 }
 
-// Within a split held in registers: the first element whose cumulative mass
-// exceeds `rem` (entries [head | groups | tail] are scanned in id order);
-// split-relative, -1 if rounding left no crossing.  Whole workgroup.
-template <int DT>
-__device__ __forceinline__ int draw_in_split(const SplitRegs<DT> &X, double rem, bool use_p, const Decision &d,
-                             Scale k, DrawLds &D) {
-  constexpr int EPV = 16 / elem_bytes(DT);
-  constexpr int VB = kVecPerThreadB;
-  const int t = threadIdx.x;
-  __shared__ int s_entry, s_token;
-  __shared__ double s_before;
-  const int nvec = X.nvec;
-  const int E = nvec + 2;
+// Mass of split-relative elements [j0, j1), one lane, scalar loads.
+template <int DT, bool TOPP, bool P>
+__device__ __forceinline__ double range_mass(const SplitGeo &g, int j0, int j1, const Decision &d,
+                                             Scale k) {
+  double acc = 0.0;
+  for (int j = j0; j < j1; ++j)
+    acc += token_mass<TOPP, P>(load_elem(g.bt, j, DT), P ? 0.f : load_elem(g.bq, j, DT), d, k);
+  return acc;
+}
+
+// Sum over the workgroup (valid in every thread); `red` holds kThreads / 64.
+__device__ __forceinline__ double block_sum(double v, double *red) {
+  v = wave_sum(v);
+  if (lane_id() == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double s = 0.0;
 #pragma unroll
-  for (int u = 0; u < VB; ++u) {
-    const int v = t + u * kThreads;
-    if (v < nvec) D.val[1 + v] = use_p ? X.cp[u] : X.cr[u];
+  for (int w = 0; w < kThreads / 64; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// Inclusive prefix sum over a wave (lanes in order).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double u = __shfl_up(v, o, 64);
+    if (l >= o) v += u;
   }
+  return v;
+}
+
+// The draw inside one split: entries (head, lanes, tail) with masses e_head,
+// e_lane (this thread's lane entry) and e_tail; the token is the first one
+// whose cumulative mass from the start of the split exceeds `rem`.  Returns
+// the split-relative token in every thread; if rounding leaves no crossing,
+// the last token with positive mass.  Whole workgroup.
+template <int DT, bool TOPP, bool P>
+__device__ int draw_split(const SplitGeo &g, double e_head, double e_lane, double e_tail,
+                          double rem, const Decision &d, Scale k, DrawLds &D) {
+  __shared__ int s_ent;
+  __shared__ double s_base;
+  const int t = threadIdx.x, l = lane_id(), w = t >> 6;
+  // 1. the crossing entry: cumulative masses head, lanes 0..255, tail
+  const double incl_w = wave_incl_scan(e_lane);
+  if (l == 63) D.wsum[w] = incl_w;
+  __syncthreads();
+  double off = e_head;
+  for (int i = 0; i < w; ++i) off += D.wsum[i];
+  const double incl = off + incl_w;
+  const double prev = l > 0 ? off + __shfl_up(incl_w, 1, 64) : off;  // cumulative before this entry
+  const uint64_t cross = __ballot(prev <= rem && rem < incl);
+  const uint64_t pos = __ballot(e_lane > 0.0);
+  if (l == 0) {
+    D.wfirst[w] = cross ? w * 64 + __builtin_ctzll(cross) : -1;
+    D.wlast[w] = pos ? w * 64 + 63 - __builtin_clzll(pos) : -1;
+  }
+  if (cross && l == __builtin_ctzll(cross)) D.wprev[w] = prev;
+  if (t == kThreads - 1) D.lanes_end = incl;
+  __syncthreads();
   if (t == 0) {
-    D.val[0] = use_p ? X.hp : X.hr;
-    D.val[1 + nvec] = use_p ? X.tp : X.tr;
-    s_entry = kNoEntry;
-    s_token = -1;
-  }
-  __syncthreads();
-  const int per = (E + kThreads - 1) / kThreads;
-  const int e0 = min(E, t * per), e1 = min(E, e0 + per);
-  double own = 0.0;
-  for (int e = e0; e < e1; ++e) own += D.val[e];
-  D.tsum[t] = own;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const double v = t >= off ? D.tsum[t - off] : 0.0;
-    __syncthreads();
-    D.tsum[t] += v;
-    __syncthreads();
-  }
-  {
-    double c = t > 0 ? D.tsum[t - 1] : 0.0;
-    for (int e = e0; e < e1; ++e) {
-      const double v = D.val[e];
-      if (c <= rem && rem < c + v) atomicMin(&s_entry, e);  // lowest entry wins
-      c += v;
-    }
-  }
-  __syncthreads();
-  const int ent = s_entry;
-  if (ent != kNoEntry && t == 0) {  // the winner's base, summed in the same order
-    const int owner = ent / per;
-    double cc = owner > 0 ? D.tsum[owner - 1] : 0.0;
-    for (int e = owner * per; e < ent; ++e) cc += D.val[e];
-    s_before = cc;
-  }
-  __syncthreads();
-  auto value = [&](float a, float q) {
-    double r, p;
-    resid_terms(a, q, d, k, r, p);
-    return use_p ? p : r;
-  };
-  if (ent != kNoEntry) {
-    const double before = s_before;
-    if (ent == 0 || ent == nvec + 1) {  // the scalar head or tail
-      if (t == 0) {
-        const int j0 = ent == 0 ? 0 : X.tail0, j1 = ent == 0 ? X.head : X.st.n;
-        double cc = before;
-        int pick = -1, last_pos = -1;
-        for (int j = j0; j < j1 && pick < 0; ++j) {
-          const double v = value(load_elem(X.st.base, j, DT), load_elem(X.sq.base, j, DT));
-          if (v > 0.0) last_pos = j;
-          cc += v;
-          if (cc > rem) pick = j;
-        }
-        s_token = pick >= 0 ? pick : last_pos;
-      }
+    int ent = -1;
+    double base = 0.0;
+    if (rem < e_head) {
+      ent = 0;
     } else {
-      const int v = ent - 1;
-      if (t == v % kThreads) {
-        const int uu = v / kThreads;
-        double cc = before;
-        int pick = -1, last_pos = -1;
-        // constant register indexes only: the scan is unrolled per group slot
-#pragma unroll
-        for (int u = 0; u < VB; ++u) {
-          if (u == uu) {
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-              const double val = value(vec_elem(X.wt[u], e, DT), vec_elem(X.wq[u], e, DT));
-              const int j = X.head + v * EPV + e;
-              if (pick < 0) {
-                if (val > 0.0) last_pos = j;
-                cc += val;
-                if (cc > rem) pick = j;
-              }
-            }
-          }
+      for (int i = 0; i < kThreads / 64 && ent < 0; ++i)
+        if (D.wfirst[i] >= 0) {
+          ent = 1 + D.wfirst[i];
+          base = D.wprev[i];
         }
-        s_token = pick >= 0 ? pick : last_pos;
+      if (ent < 0 && rem < D.lanes_end + e_tail) {
+        ent = kThreads + 1;
+        base = D.lanes_end;
       }
     }
+    if (ent < 0) {  // rounding: no crossing; the last entry with mass, walked to its end
+      if (e_tail > 0.0) ent = kThreads + 1;
+      for (int i = kThreads / 64 - 1; i >= 0 && ent < 0; --i)
+        if (D.wlast[i] >= 0) ent = 1 + D.wlast[i];
+      if (ent < 0) ent = 0;
+      base = -INFINITY;  // never crosses: the walk keeps the last token with mass
+    }
+    s_ent = ent;
+    s_base = base;
   }
   __syncthreads();
-  return s_token;
+  const int ent = s_ent;
+  // 2. the walk: one wave, one token per lane, an inclusive scan of the masses
+  __shared__ int s_tok;
+  if (w == 0) {
+    int j0, j1;
+    entry_range<DT>(g, ent, j0, j1);
+    const int j = j0 + l;
+    const bool in = j < j1;
+    const double v = in ? token_mass<TOPP, P>(load_elem(g.bt, j, DT), P ? 0.f : load_elem(g.bq, j, DT), d, k) : 0.0;
+    const double c = s_base + wave_incl_scan(v);
+    const uint64_t hit = __ballot(in && c > rem);
+    const uint64_t has = __ballot(in && v > 0.0);
+    if (l == 0)
+      s_tok = hit ? j0 + __builtin_ctzll(hit) : has ? j0 + 63 - __builtin_clzll(has) : -1;
+  }
+  __syncthreads();
+  return s_tok;
 }
 
-template <int DT>
+template <int DT, bool TOPP>
 __device__ void residual_tile(const char *target, const char *draft, const int32_t *tokens,
                               const float *u_accept, const float *u_sample, int B, int K, int V,
                               int S, int SB, double k64, Scale k, u64 epoch,
                               const u64 *part_m, const u64 *part_z, const u64 *part_x,
-                              const RowStat *rowstat, ResidPart *rpart, int32_t *out_accepted,
-                              int32_t *out_tokens, float *out_p, float *out_q, float *out_mass,
-                              int b, int s) {
+                              const RowStat *rowstat, u64 *rtot, u64 *rent,
+                              int32_t *out_accepted, int32_t *out_tokens, float *out_p,
+                              float *out_q, float *out_mass, int b, int s, ResidLds &R) {
   const int t = threadIdx.x;
-  __shared__ TileLds lds;
-  __shared__ Decision sdec;
-  __shared__ int s_ok, s_split, s_use_p, s_fb_token;
-  __shared__ double s_rem, s_total;
-  __shared__ double red_r[kThreads / 64], red_p[kThreads / 64];
-  __shared__ int red_lr[kThreads / 64], red_lp[kThreads / 64];
+  TileLds &lds = R.lds;
+  Decision &sdec = R.dec;
+  int &s_ok = R.ok, &s_split = R.split, &s_use_p = R.use_p;
+  double &s_rem = R.rem, &s_total = R.total;
+  double *red = R.red;
 
   // 1. decide, once every streaming tile of request b has published
-  if (!decide(tokens, u_accept, B, K, S, k64, part_m, part_z, part_x, epoch,
-                  rowstat, b, s == 0, out_accepted, out_tokens, out_p, out_q, lds.dec, &sdec,
-                  &s_ok)) {
+  if (!decide(tokens, u_accept, B, K, S, k64, k, part_m, part_z, part_x, epoch, rowstat, b,
+              s == 0, out_accepted, out_tokens, out_p, out_q, lds.dec, &sdec, &s_ok)) {
     if (t == 0) out_accepted[b] = -2;  // time-out: flag the request as failed
     return;
   }
@@ -466,70 +474,40 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
   const char *rt = row_ptr(target, (size_t)b * (K + 1) + d.n, V, DT);
   const char *rd = d.mode == kModeResidual ? row_ptr(draft, (size_t)b * K + d.n, V, DT) : rt;
 
-  // 2. the residual mass of split s, published as one record
+  // 2. the residual masses of split s: its entries, then its total
   {
-    SplitRegs<DT> X;
-    load_split<DT>(X, rt, rd, V, s, d, k);
-    double own_r = X.hr + X.tr, own_p = X.hp + X.tp;
-#pragma unroll
-    for (int u = 0; u < kVecPerThreadB; ++u) {
-      own_r += X.cr[u];
-      own_p += X.cp[u];
-    }
-    own_r = wave_sum(own_r);
-    own_p = wave_sum(own_p);
-    int wl_r = X.lr, wl_p = X.lp;
-    for (int o = 32; o > 0; o >>= 1) {
-      wl_r = max(wl_r, __shfl_xor(wl_r, o, 64));
-      wl_p = max(wl_p, __shfl_xor(wl_p, o, 64));
-    }
-    if (lane_id() == 0) {
-      red_r[t >> 6] = own_r;
-      red_p[t >> 6] = own_p;
-      red_lr[t >> 6] = wl_r;
-      red_lp[t >> 6] = wl_p;
-    }
-    __syncthreads();
+    const SplitGeo g = split_geo<DT>(rt, rd, V, s);
+    const double lm = lane_mass<DT, TOPP, false>(g, d, k);
+    double hm = 0.0, tm = 0.0;
     if (t == 0) {
-      double R2 = 0.0, P2 = 0.0;
-      int LR = -1, LP = -1;
-      for (int w = 0; w < kThreads / 64; ++w) {
-        R2 += red_r[w];
-        P2 += red_p[w];
-        LR = max(LR, red_lr[w]);
-        LP = max(LP, red_lp[w]);
-      }
-      ResidPart *out = rpart + (size_t)b * SB + s;
-      store_agent(&out->r, pack_f64(R2, epoch));
-      store_agent(&out->p, pack_f64(P2, epoch));
-      store_agent(&out->idx, pack_idx2(LR, LP, epoch));
+      hm = range_mass<DT, TOPP, false>(g, 0, g.head, d, k);
+      tm = range_mass<DT, TOPP, false>(g, g.tail0, g.n, d, k);
     }
+    u64 *ent = rent + ((size_t)b * SB + s) * kEntriesB;
+    store_agent(&ent[1 + t], pack_f64(lm, epoch));
+    if (t == 0) {
+      store_agent(&ent[0], pack_f64(hm, epoch));
+      store_agent(&ent[kThreads + 1], pack_f64(tm, epoch));
+    }
+    const double tot = block_sum(lm + hm + tm, red);
+    if (t == 0) store_agent(&rtot[(size_t)b * SB + s], pack_f64(tot, epoch));
   }
   // only the request's last residual tile (dispatched after its siblings)
   // gathers the split masses and draws
   if (s != SB - 1) return;
 
-  // 3. the draw: which split holds u * S?
+  // 3. which split holds u * S?
   DrawLds &D = lds.draw;
   {
     bool ok = true;
-    const ResidPart *rp = rpart + (size_t)b * SB;
     for (int i = t; i < SB; i += kThreads) {
       bool got = false;
+      double v = 0.0;
       for (int it = 0; it < kSpinLimit && !got; ++it) {
-        const u64 rw = load_agent(&rp[i].r), pw = load_agent(&rp[i].p), iw = load_agent(&rp[i].idx);
-        double rv, pv;
-        int a, c;
-        got = unpack_f64(rw, epoch, &rv) & unpack_f64(pw, epoch, &pv) & unpack_idx2(iw, epoch, &a, &c);
-        if (got) {
-          D.pr[i] = rv;
-          D.pp[i] = pv;
-          D.plr[i] = a >= 0 ? i * split_elems_b(DT) + a : -1;
-          D.plp[i] = c >= 0 ? i * split_elems_b(DT) + c : -1;
-        } else {
-          spin_pause();
-        }
+        got = unpack_f64(load_agent(&rtot[(size_t)b * SB + i]), epoch, &v);
+        if (!got) spin_pause();
       }
+      D.tot[i] = v;
       ok = ok && got;
     }
     if (t == 0) s_ok = 1;
@@ -541,47 +519,96 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
       return;
     }
   }
+  // S <= 0 cannot happen in exact arithmetic after a rejection (the residual
+  // holds at least q'(x) - p'(x) > 0); it can when p' and q' agree and the
+  // draft token has no mass under either.  Then the draw falls back to p'
+  // (recomputed here: split by split, rare and slow).
   if (t == 0) {
-    double Sr = 0.0;
-    for (int i = 0; i < SB; ++i) Sr += D.pr[i];
-    int use_p = 0;
-    double tot = Sr;
-    if (!(Sr > 0.0)) {  // unreachable in exact arithmetic after a rejection
-      use_p = 1;
-      tot = 0.0;
-      for (int i = 0; i < SB; ++i) tot += D.pp[i];
+    double tot = 0.0;
+    for (int i = 0; i < SB; ++i) tot += D.tot[i];
+    s_use_p = !(tot > 0.0);
+  }
+  __syncthreads();
+  if (s_use_p) {
+    for (int i = 0; i < SB; ++i) {
+      const SplitGeo g = split_geo<DT>(rt, rd, V, i);
+      double v = lane_mass<DT, TOPP, true>(g, d, k);
+      if (t == 0)
+        v += range_mass<DT, TOPP, true>(g, 0, g.head, d, k) +
+             range_mass<DT, TOPP, true>(g, g.tail0, g.n, d, k);
+      v = block_sum(v, red);
+      if (t == 0) D.tot[i] = v;
     }
+    __syncthreads();
+  }
+  if (t == 0) {
+    double tot = 0.0;
+    for (int i = 0; i < SB; ++i) tot += D.tot[i];
     const double goal = (double)u_sample[b] * tot;
     double c = 0.0;
-    int split = -1;
-    for (int i = 0; i < SB; ++i) {
-      const double v = use_p ? D.pp[i] : D.pr[i];
-      if (c + v > goal) {
-        split = i;
-        break;
-      }
-      c += v;
+    int split = -1, last = -1;
+    for (int i = 0; i < SB && split < 0; ++i) {
+      if (D.tot[i] > 0.0) last = i;
+      if (c + D.tot[i] > goal) split = i;
+      else c += D.tot[i];
     }
-    int fb = -1;  // rounding left no crossing: the last token with mass
-    if (split < 0)
-      for (int i = SB - 1; i >= 0 && fb < 0; --i) fb = use_p ? D.plp[i] : D.plr[i];
+    if (split < 0) {  // rounding: no crossing; the last split with mass, to its end
+      split = last;
+      c = -INFINITY;
+    }
     s_split = split;
-    s_use_p = use_p;
     s_rem = goal - c;
     s_total = tot;
-    s_fb_token = split >= 0 ? (use_p ? D.plp[split] : D.plr[split]) : fb;
   }
   __syncthreads();
   const int split = s_split;
-  int tok = s_fb_token;
+  int tok = -1;
   if (split >= 0) {
-    // the crossing split is read again (it is this tile's own split only one
-    // time in SB; keeping that one in registers would cost every tile of the
-    // kernel occupancy)
-    SplitRegs<DT> Y;
-    load_split<DT>(Y, rt, rd, V, split, d, k);
-    const int local = draw_in_split<DT>(Y, s_rem, s_use_p != 0, d, k, D);
-    if (local >= 0) tok = Y.st.e0 + local;
+    // 4. the entries of the crossing split, then the walk
+    const SplitGeo g = split_geo<DT>(rt, rd, V, split);
+    double eh = 0.0, el = 0.0, et = 0.0;
+    int local;
+    if (!s_use_p) {
+      const u64 *ent = rent + ((size_t)b * SB + split) * kEntriesB;
+      bool got = false;
+      for (int it = 0; it < kSpinLimit && !got; ++it) {
+        got = unpack_f64(load_agent(&ent[1 + t]), epoch, &el);
+        if (t == 0) {
+          got = got & unpack_f64(load_agent(&ent[0]), epoch, &eh) &
+                unpack_f64(load_agent(&ent[kThreads + 1]), epoch, &et);
+        }
+        if (!got) spin_pause();
+      }
+      if (t == 0) s_ok = 1;
+      __syncthreads();
+      if (!got) s_ok = 0;
+      __syncthreads();
+      if (!s_ok) {
+        if (t == 0) out_accepted[b] = -2;
+        return;
+      }
+      if (t == 0) {  // thread 0 holds head / tail
+        D.wsum[0] = eh;
+        D.wsum[1] = et;
+      }
+      __syncthreads();
+      eh = D.wsum[0];
+      et = D.wsum[1];
+      __syncthreads();
+      local = draw_split<DT, TOPP, false>(g, eh, el, et, s_rem, d, k, D);
+    } else {
+      el = lane_mass<DT, TOPP, true>(g, d, k);
+      if (t == 0) {
+        D.wsum[0] = range_mass<DT, TOPP, true>(g, 0, g.head, d, k);
+        D.wsum[1] = range_mass<DT, TOPP, true>(g, g.tail0, g.n, d, k);
+      }
+      __syncthreads();
+      eh = D.wsum[0];
+      et = D.wsum[1];
+      __syncthreads();
+      local = draw_split<DT, TOPP, true>(g, eh, el, et, s_rem, d, k, D);
+    }
+    if (local >= 0) tok = g.e0 + local;
   }
   if (t == 0) {
     out_tokens[(size_t)b * (K + 1) + d.n] = tok;
@@ -597,7 +624,8 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
     const float *__restrict__ u_sample, int B, int K, int V, int S, int SB, double k64, Scale k,
     u64 epoch, int phase, int lag, u64 *__restrict__ part_m, u64 *__restrict__ part_z,
-    u64 *__restrict__ part_x, const RowStat *__restrict__ rowstat, ResidPart *__restrict__ rpart,
+    u64 *__restrict__ part_x, const RowStat *__restrict__ rowstat, u64 *__restrict__ rtot,
+    u64 *__restrict__ rent,
     int32_t *__restrict__ out_accepted, int32_t *__restrict__ out_tokens,
     float *__restrict__ out_p, float *__restrict__ out_q, float *__restrict__ out_mass) {
   const int blk = (int)blockIdx.x;
@@ -673,16 +701,22 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     }
     return;
   }
-  residual_tile<DT>(target, draft, tokens, u_accept, u_sample, B, K, V, S, SB, k64, k, epoch,
-                    part_m, part_z, part_x, rowstat, rpart, out_accepted, out_tokens, out_p,
-                    out_q, out_mass, b, idx);
+  __shared__ ResidLds rl;
+  if (rowstat)
+    residual_tile<DT, true>(target, draft, tokens, u_accept, u_sample, B, K, V, S, SB, k64, k,
+                            epoch, part_m, part_z, part_x, rowstat, rtot, rent, out_accepted,
+                            out_tokens, out_p, out_q, out_mass, b, idx, rl);
+  else
+    residual_tile<DT, false>(target, draft, tokens, u_accept, u_sample, B, K, V, S, SB, k64, k,
+                             epoch, part_m, part_z, part_x, rowstat, rtot, rent, out_accepted,
+                             out_tokens, out_p, out_q, out_mass, b, idx, rl);
 }
 
 hipError_t launch_sample(const void *target, const void *draft, int dtype, const int32_t *tokens,
                          const float *u_accept, const float *u_sample, int B, int K, int V,
                          int S, int SB, double k64, Scale k, u64 epoch, int phase, int lag,
                          u64 *part_m, u64 *part_z, u64 *part_x, const RowStat *rowstat,
-                         ResidPart *rpart, int32_t *out_accepted, int32_t *out_tokens,
+                         u64 *rtot, u64 *rent, int32_t *out_accepted, int32_t *out_tokens,
                          float *out_p, float *out_q, float *out_mass, hipStream_t stream) {
   const int nA = B * (2 * K + 1) * S;
   const int nB = B * SB;
@@ -693,12 +727,12 @@ hipError_t launch_sample(const void *target, const void *draft, int dtype, const
     hipLaunchKernelGGL(k_sample_fused<kBF16>, dim3(blocks), dim3(kThreads), 0, stream,
                        (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
                        K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, part_x, rowstat,
-                       rpart, out_accepted, out_tokens, out_p, out_q, out_mass);
+                       rtot, rent, out_accepted, out_tokens, out_p, out_q, out_mass);
   else
     hipLaunchKernelGGL(k_sample_fused<kF32>, dim3(blocks), dim3(kThreads), 0, stream,
                        (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
                        K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, part_x, rowstat,
-                       rpart, out_accepted, out_tokens, out_p, out_q, out_mass);
+                       rtot, rent, out_accepted, out_tokens, out_p, out_q, out_mass);
   return hipGetLastError();
 }
 
