@@ -139,10 +139,11 @@ __device__ bool decide(const int32_t *tokens, const float *u_accept, int B, int 
   // the draft tokens (for the emitted prefix) and their logits (lanes < K):
   // the logits come from the streaming tiles, -inf for a token out of range
   int x = -1;
-  float lt = -INFINITY, ld = -INFINITY;
+  float lt = -INFINITY, ld = -INFINITY, ua = 0.f;
   bool got_x = true;
   if (t < K) {
     x = tokens[(size_t)b * K + t];
+    ua = u_accept[(size_t)b * K + t];  // issued early: off the critical path
     const u64 *px = part_x + ((size_t)b * K + t) * 2;
     got_x = false;
     for (int it = 0; it < kSpinLimit && !got_x; ++it) {
@@ -219,7 +220,7 @@ __device__ bool decide(const int32_t *tokens, const float *u_accept, int B, int 
     if (i < K) {
       const double p = prob_at(lt, L.row_m[i], L.row_tau[i], L.row_zk[i], k64);
       const double q = prob_at(ld, L.row_m[K + 1 + i], L.row_tau[K + 1 + i], L.row_zk[K + 1 + i], k64);
-      accept = (double)u_accept[(size_t)b * K + i] * q < p;
+      accept = (double)ua * q < p;
       if (write_outputs && out_p) out_p[(size_t)b * K + i] = (float)p;
       if (write_outputs && out_q) out_q[(size_t)b * K + i] = (float)q;
     }
@@ -458,6 +459,7 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
                               int32_t *out_accepted, int32_t *out_tokens, float *out_p,
                               float *out_q, float *out_mass, int b, int s, ResidLds &R) {
   const int t = threadIdx.x;
+  const float us = s == SB - 1 ? u_sample[b] : 0.f;  // the drawing tile's uniform, issued early
   TileLds &lds = R.lds;
   Decision &sdec = R.dec;
   int &s_ok = R.ok, &s_split = R.split, &s_use_p = R.use_p;
@@ -544,7 +546,7 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
   if (t == 0) {
     double tot = 0.0;
     for (int i = 0; i < SB; ++i) tot += D.tot[i];
-    const double goal = (double)u_sample[b] * tot;
+    const double goal = (double)us * tot;
     double c = 0.0;
     int split = -1, last = -1;
     for (int i = 0; i < SB && split < 0; ++i) {
