@@ -23,6 +23,7 @@ constexpr int kTopThreads = 512;
 constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kBins = 256;
 constexpr float kBinsPerLog2 = 8.f;
+constexpr int kCand = 4096;  // keys of the selected bin held in LDS
 
 namespace {
 
@@ -89,6 +90,8 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(
   __shared__ unsigned s_prefix;
   __shared__ float s_tau;
   __shared__ double s_kept;
+  __shared__ uint32_t cand[kCand];
+  __shared__ unsigned s_ncand;
 
   if (t == 0) {  // the streaming kernel has completed: every partial is in place
     const u64 *pm = part_m + (size_t)row * S;
@@ -117,10 +120,22 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(
   const double goal = top_p * Z;
   const float kr = (k.hi + k.lo) * kBinsPerLog2;
 
-  // 1. mass by distance bin
-  for_row<DT>(rp, V, [&](int, float x) {
-    atomicAdd(&hist[w][dist_bin(x, M, kr)], (double)tempered(x, M, k));
-  });
+  // 1. mass by distance bin; the last bin (everything beyond it, where most
+  //    of a long tail sits) is summed in registers instead of LDS atomics
+  {
+    double far = 0.0;
+    for_row<DT>(rp, V, [&](int, float x) {
+      const int bin = dist_bin(x, M, kr);
+      const double tm = (double)tempered(x, M, k);
+      if (bin < kBins - 1)
+        atomicAdd(&hist[w][bin], tm);
+      else
+        far += tm;
+    });
+    far = wave_sum(far);
+    __syncthreads();
+    if ((t & 63) == 0) hist[w][kBins - 1] += far;
+  }
   __syncthreads();
   if (t < kBins) {
     double s = 0.0;
@@ -147,8 +162,25 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(
   }
   __syncthreads();
 
-  // 2. exact cut inside the selected bin: radix rounds over value keys
+  // 2. the selected bin's elements, gathered into LDS as value keys (one
+  //    more pass over the row); if they do not fit, the rounds below read
+  //    the row again each time
   const int sel = s_bin;
+  if (!s_done) {
+    if (t == 0) s_ncand = 0;
+    __syncthreads();
+    for_row<DT>(rp, V, [&](int, float x) {
+      if (dist_bin(x, M, kr) != sel) return;
+      const unsigned slot = atomicAdd(&s_ncand, 1u);
+      if (slot < (unsigned)kCand) cand[slot] = key_of_f32(x);
+    });
+    __syncthreads();
+  }
+  const unsigned ncand = s_ncand;
+  const bool in_lds = ncand <= (unsigned)kCand;
+
+  // 3. exact cut inside the selected bin: radix rounds over value keys,
+  //    accumulating mass from the top
   for (int shift = 24; shift >= 0 && !s_done; shift -= 8) {
     if (t < kBins) {
       mass[t] = 0.0;
@@ -158,16 +190,21 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(
     }
     __syncthreads();
     const unsigned prefix = s_prefix;
-    for_row<DT>(rp, V, [&](int, float x) {
-      if (dist_bin(x, M, kr) != sel) return;
-      const uint32_t key = key_of_f32(x);
+    auto visit = [&](uint32_t key) {
       if (shift < 24 && (key >> (shift + 8)) != prefix) return;
       const int sb = (key >> shift) & 0xFF;
-      atomicAdd(&mass[sb], (double)tempered(x, M, k));
+      atomicAdd(&mass[sb], (double)tempered(f32_of_key(key), M, k));
       atomicAdd(&cnt[sb], 1u);
       atomicMin(&kmin[sb], key);
       atomicMax(&kmax[sb], key);
-    });
+    };
+    if (in_lds) {
+      for (unsigned i = t; i < ncand; i += kTopThreads) visit(cand[i]);
+    } else {
+      for_row<DT>(rp, V, [&](int, float x) {
+        if (dist_bin(x, M, kr) == sel) visit(key_of_f32(x));
+      });
+    }
     __syncthreads();
     if (t == 0) {
       double above = s_above;
