@@ -52,6 +52,8 @@ def lib():
         L.oracle_row_distribution.restype = I
         L.oracle_tree_is_valid.argtypes = [P, P, I]
         L.oracle_tree_is_valid.restype = I
+        L.oracle_kv_commit.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, I, P]
+        L.oracle_kv_commit.restype = I
         _lib = L
     return _lib
 
@@ -154,6 +156,33 @@ def tree_is_valid(parents, anc_mask) -> bool:
     if rc < 0:
         raise ValueError("oracle_tree_is_valid: bad arguments")
     return bool(rc)
+
+
+def kv_commit(kv, cache_len, path_len, path_nodes=None, N=None, mirror=None):
+    """KV-cache commit (oracle.c, oracle_kv_commit).  kv [L, 2, B, H, S, D]
+    (any dtype: bytes are copied); path_nodes [B, N] int32 or None (linear:
+    positions 1..d).  Returns (kv after, mirror after or None, new_len)."""
+    kv = np.ascontiguousarray(kv)
+    L, two, B, H, S, D = kv.shape
+    assert two == 2
+    cache_len = np.ascontiguousarray(cache_len, np.int32)
+    path_len = np.ascontiguousarray(path_len, np.int32)
+    if path_nodes is not None:
+        path_nodes = np.ascontiguousarray(path_nodes, np.int32)
+        N = path_nodes.shape[1]
+        assert path_nodes.shape == (B, N)
+    assert N is not None and cache_len.shape == (B,) and path_len.shape == (B,)
+    out = kv.copy()
+    mout = None
+    if mirror is not None:
+        mout = np.ascontiguousarray(mirror).copy()
+        assert mout.shape == kv.shape and mout.dtype == kv.dtype
+    new_len = np.empty(B, np.int32)
+    rc = lib().oracle_kv_commit(_p(kv), _p(out), _p(mout), kv.dtype.itemsize, L, B, H, S, D,
+                                _p(cache_len), _p(path_len), _p(path_nodes), int(N), _p(new_len))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_commit: {rc}")
+    return out, mout, new_len
 
 
 def verify_workload(w):

@@ -497,3 +497,72 @@ int oracle_verify_tree(const void *target, int dtype, const int32_t *parents,
   free(a); free(match); free(acc); free(depth);
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * KV-cache commit after one cycle.  Both models keep their own cache; the
+ * entries of rejected drafts are cut away before the next cycle (LOTOOK,
+ * section on the KV cache), and a drafter that shares the target's layers
+ * has its temporary entries overwritten with the target's values (SubSpec
+ * review, Method part 2, step 4 "Update KV").  For a merged tree verified in
+ * one pass (TAPS, "방법론") the accepted path's entries are gathered into
+ * consecutive slots.
+ *
+ * Cache layout [L][2][B][H][S][D], elements of es bytes (the bytes are
+ * copied, never interpreted).  Request b's cycle wrote its entries at slots
+ * c .. c+N-1 (c = cache_len[b]): slot c + i holds node i of the tree, or
+ * position i of a linear draft (node / position 0 is the root, the token
+ * emitted by the previous cycle).  The accepted path is the root and then
+ * path_nodes[b][0 .. d-1] (d = path_len[b]), or positions 1 .. d when
+ * path_nodes is NULL.  After the commit slot c + j holds the entry of path
+ * element j (j = 0 .. d), every other slot is unchanged, and new_len[b] =
+ * c + 1 + d.  Definition is out of place: every committed entry is the
+ * cache's entry before the call.  The mirror, if given, receives the same
+ * d + 1 entries at the same slots.
+ *
+ * A request whose inputs are inconsistent (d outside [0, N-1], c < 0,
+ * c + N > S, or path nodes not strictly increasing within [1, N-1]) is left
+ * untouched and gets new_len[b] = -1.
+ *
+ * kv_out (and mirror_out) must hold a copy of the cache (and mirror) before
+ * the call; kv_in is the cache before the call.
+ * ------------------------------------------------------------------------ */
+int oracle_kv_commit(const void *kv_in, void *kv_out, void *mirror_out, int es, int L, int B,
+                     int H, int S, int D, const int32_t *cache_len, const int32_t *path_len,
+                     const int32_t *path_nodes, int N, int32_t *new_len) {
+  if (!kv_in || !kv_out || !cache_len || !path_len || !new_len) return -1;
+  if (es < 1 || L < 1 || B < 1 || H < 1 || S < 1 || D < 1 || N < 1) return -2;
+  const size_t row = (size_t)D * (size_t)es;
+  const unsigned char *src = (const unsigned char *)kv_in;
+  unsigned char *dst = (unsigned char *)kv_out;
+  unsigned char *mir = (unsigned char *)mirror_out;
+  for (int b = 0; b < B; ++b) {
+    const int c = cache_len[b];
+    const int d = path_len[b];
+    int ok = d >= 0 && d <= N - 1 && c >= 0 && (long)c + N <= S;
+    if (ok && path_nodes) {
+      int prev = 0;
+      for (int j = 0; j < d && ok; ++j) {
+        const int p = path_nodes[(size_t)b * N + j];
+        if (p <= prev || p > N - 1) ok = 0;
+        prev = p;
+      }
+    }
+    if (!ok) {
+      new_len[b] = -1;
+      continue;
+    }
+    for (int l = 0; l < L; ++l)
+      for (int kv = 0; kv < 2; ++kv)
+        for (int h = 0; h < H; ++h) {
+          const size_t base = ((((size_t)l * 2 + kv) * B + b) * H + h) * (size_t)S * row;
+          for (int j = 0; j <= d; ++j) {
+            const int node = j == 0 ? 0 : (path_nodes ? path_nodes[(size_t)b * N + j - 1] : j);
+            const unsigned char *from = src + base + (size_t)(c + node) * row;
+            memcpy(dst + base + (size_t)(c + j) * row, from, row);
+            if (mir) memcpy(mir + base + (size_t)(c + j) * row, from, row);
+          }
+        }
+    new_len[b] = c + 1 + d;
+  }
+  return 0;
+}

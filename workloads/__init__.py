@@ -357,3 +357,64 @@ def subset(w: "Workload", requests) -> "Workload":
         if v is not None:
             kw[name] = v[r]
     return dataclasses.replace(w, **kw)
+
+
+@dataclasses.dataclass
+class KVWorkload:
+    """A KV-cache commit: cache [L, 2, B, H, S, D] of 16-bit words (each
+    row distinct), per-request committed length, and the accepted path of
+    the cycle (tree node ids by depth, or None for a linear draft)."""
+    name: str
+    kv: np.ndarray
+    cache_len: np.ndarray
+    path_len: np.ndarray
+    path_nodes: Optional[np.ndarray]
+    N: int
+    mirror: Optional[np.ndarray]
+
+    @property
+    def shape(self):
+        return self.kv.shape
+
+
+def random_paths(rng: np.random.Generator, B: int, n_per_tree: int):
+    """Accepted paths in merged trees of 2 n_per_tree + 1 nodes: per request
+    a random node of a random merged tree, the path being its ancestors below
+    the root and itself, by depth.  Returns (path_len[B], path_nodes[B, N])."""
+    N = 2 * n_per_tree + 1
+    plen = np.zeros(B, np.int32)
+    nodes = np.full((B, N), -1, np.int32)
+    for b in range(B):
+        p1 = grow_tree(rng, n_per_tree)
+        p2 = grow_tree(rng, n_per_tree)
+        zeros = np.zeros(n_per_tree + 1, np.int32)
+        par, _, _ = merge_two_trees(p1, zeros, ancestor_mask(p1), p2, zeros, ancestor_mask(p2))
+        node = int(rng.integers(N))
+        chain = []
+        while node > 0:
+            chain.append(node)
+            node = int(par[node])
+        chain.reverse()
+        plen[b] = len(chain)
+        nodes[b, :len(chain)] = chain
+    return plen, nodes
+
+
+def kv_commit_workload(seed: int = 0, L: int = 32, B: int = 32, H: int = 8, S: int = 256,
+                       D: int = 128, n_per_tree: int = 31, tree: bool = True,
+                       mirror: bool = True, name: str = "kv") -> KVWorkload:
+    """Cache of a Llama-3-8B-shaped target (32 layers, 8 KV heads of 128)
+    in bf16 bits; a cycle of N = 2 n_per_tree + 1 slots (tree) or N slots of
+    a linear draft with n_per_tree accepted at most."""
+    ss = np.random.SeedSequence([20261202 + 50, seed])
+    r_kv, r_len, r_tree = [np.random.default_rng(x) for x in ss.spawn(3)]
+    N = 2 * n_per_tree + 1
+    kv = r_kv.integers(0, 1 << 16, size=(L, 2, B, H, S, D), dtype=np.uint16)
+    cache_len = r_len.integers(0, S - N + 1, size=B).astype(np.int32)
+    if tree:
+        path_len, path_nodes = random_paths(r_tree, B, n_per_tree)
+    else:
+        path_len = r_tree.integers(0, N, size=B).astype(np.int32)
+        path_nodes = None
+    mir = r_kv.integers(0, 1 << 16, size=kv.shape, dtype=np.uint16) if mirror else None
+    return KVWorkload(name, kv, cache_len, path_len, path_nodes, N, mir)
