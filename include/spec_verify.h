@@ -77,9 +77,9 @@ enum {
   SPEC_OK = 0,
   SPEC_ERR_NULL = -1,      /* a required pointer is NULL */
   SPEC_ERR_SHAPE = -2,     /* B, K, N or V out of range */
-  SPEC_ERR_PARAM = -3,     /* temperature not finite / <= 0, top_p not in (0, 1], bad dtype or op */
+  SPEC_ERR_PARAM = -3,     /* temperature not finite / <= 0, top_p not in (0, 1], bad dtype, op or element size */
   SPEC_ERR_WORKSPACE = -4, /* workspace smaller than spec_verify_workspace_bytes() */
-  SPEC_ERR_ALIGN = -5,     /* workspace not 256-byte aligned, or logits not element aligned */
+  SPEC_ERR_ALIGN = -5,     /* workspace not 256-byte aligned, logits not element aligned, or a cache row / base not 16-byte aligned */
   SPEC_ERR_HIP = -6        /* a HIP launch or runtime call failed */
 };
 
@@ -135,6 +135,31 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parent
                      int V, int32_t *out_path_len, int32_t *out_path_nodes,
                      int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/* KV-cache commit after one cycle (next to the verify: the entries of
+ * rejected drafts are cut away; lotook.com explainer, section on the KV
+ * cache; a drafter sharing the target's layers receives the target's entries,
+ * SubSpec review, Method part 2, step 4; a merged tree keeps its longest
+ * accepted path, TAPS, "방법론").
+ *   kv [L, 2, B, H, S, D] device buffer, elements of elem_bytes (1, 2, 4 or
+ *     8; only bytes are moved), D * elem_bytes a multiple of 16, 16-byte
+ *     aligned.  Request b's cycle wrote its N entries at slots c .. c+N-1,
+ *     c = cache_len[b]: slot c + i holds tree node i (or linear position i);
+ *     node 0 is the root (the token emitted by the previous cycle).
+ *   path_len [B] = d (out_path_len of spec_verify_tree, or out_accepted of
+ *     the linear calls); path_nodes [B, N] (out_path_nodes of
+ *     spec_verify_tree), or NULL for a linear draft (positions 1 .. d).
+ *   After the call slot c + j holds path element j (j = 0 .. d: the root,
+ *   then the path by depth); other slots are unchanged; new_len[b] =
+ *   c + 1 + d.  mirror (NULL or a second cache of the same layout, not kv)
+ *   receives the same d + 1 entries at the same slots.
+ *   A request with d outside [0, N-1], c < 0, c + N > S, or path nodes not
+ *   strictly increasing within [1, N-1] is left untouched and gets
+ *   new_len[b] = -1 (this includes d = -2, a verify that timed out).
+ *   Limits: 1 <= N <= 64, N <= S, N * D * elem_bytes <= 32768. */
+int spec_kv_commit(void *kv, void *mirror, int elem_bytes, int L, int B, int H, int S, int D,
+                   const int32_t *cache_len, const int32_t *path_len,
+                   const int32_t *path_nodes, int N, int32_t *new_len, hipStream_t stream);
 
 /* Static description of a status code (host). */
 const char *spec_status_string(int status);

@@ -8,7 +8,7 @@ current HIP stream.  If the library has not been built the calls raise: there
 is no fallback implementation.
 
 Entry points (same names as the C ABI, minus the ``spec_`` prefix):
-``verify_greedy``, ``verify_sample``, ``verify_tree``,
+``verify_greedy``, ``verify_sample``, ``verify_tree``, ``kv_commit``,
 ``verify_workspace_bytes``, ``status_string``, ``profile_begin``,
 ``profile_end``.
 """
@@ -28,7 +28,8 @@ ERRORS = {-1: "SPEC_ERR_NULL", -2: "SPEC_ERR_SHAPE", -3: "SPEC_ERR_PARAM",
           -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_ALIGN", -6: "SPEC_ERR_HIP"}
 
 EXPORTS = ("spec_verify_workspace_bytes", "spec_verify_greedy", "spec_verify_sample",
-           "spec_verify_tree", "spec_status_string", "spec_profile_begin", "spec_profile_end")
+           "spec_verify_tree", "spec_kv_commit", "spec_status_string", "spec_profile_begin",
+           "spec_profile_end")
 
 _lib = None
 
@@ -58,6 +59,8 @@ def load() -> ctypes.CDLL:
     L.spec_verify_sample.restype = I
     L.spec_verify_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, Z, P]
     L.spec_verify_tree.restype = I
+    L.spec_kv_commit.argtypes = [P, P, I, I, I, I, I, I, P, P, P, I, P, P]
+    L.spec_kv_commit.restype = I
     L.spec_status_string.argtypes = [I]
     L.spec_status_string.restype = ctypes.c_char_p
     L.spec_profile_begin.argtypes = [I]
@@ -230,6 +233,37 @@ def verify_tree(target, parents, node_tokens, anc_mask, *, workspace=None,
     if rc != SPEC_OK:
         raise SpecVerifyError(rc, "spec_verify_tree")
     return out
+
+
+def kv_commit(kv, cache_len, path_len, path_nodes=None, *, N: Optional[int] = None,
+              mirror=None, stream=None, out=None):
+    """KV-cache commit after a cycle.  kv [L, 2, B, H, S, D] (any dtype; only
+    bytes move), cache_len / path_len [B] int32, path_nodes [B, N] int32 or
+    None (linear draft: give N).  Updates kv (and mirror) in place on the
+    stream; returns new_len [B] int32."""
+    torch = _torch()
+    if kv.dim() != 6 or kv.shape[1] != 2:
+        raise ValueError(f"kv must be [L, 2, B, H, S, D], got {tuple(kv.shape)}")
+    L, _, B, H, S, D = kv.shape
+    dev = kv.device
+    _check(kv, "kv", kv.shape, device=dev)
+    _check(cache_len, "cache_len", (B,), torch.int32, dev)
+    _check(path_len, "path_len", (B,), torch.int32, dev)
+    if path_nodes is not None:
+        N = path_nodes.shape[1]
+        _check(path_nodes, "path_nodes", (B, N), torch.int32, dev)
+    if N is None:
+        raise ValueError("N is required for a linear draft (path_nodes=None)")
+    if mirror is not None:
+        _check(mirror, "mirror", kv.shape, kv.dtype, dev)
+    new_len = out if out is not None else torch.empty(B, dtype=torch.int32, device=dev)
+    _check(new_len, "out new_len", (B,), torch.int32, dev)
+    rc = load().spec_kv_commit(_ptr(kv), _ptr(mirror), kv.element_size(), L, B, H, S, D,
+                               _ptr(cache_len), _ptr(path_len), _ptr(path_nodes), int(N),
+                               _ptr(new_len), _stream(dev, stream))
+    if rc != SPEC_OK:
+        raise SpecVerifyError(rc, "spec_kv_commit")
+    return new_len
 
 
 def profile_begin(max_launches: int) -> None:

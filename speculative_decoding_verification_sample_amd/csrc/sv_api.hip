@@ -1,6 +1,7 @@
 // extern "C" entry points of libspecverify.so (declared in include/spec_verify.h).
 // Every argument is validated on the host before the first HIP call, so an
 // invalid call returns an error code with nothing enqueued.
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cmath>
@@ -213,6 +214,30 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parent
                       stream) != hipSuccess)
     return SPEC_ERR_HIP;
   prof_after(stream);
+  return SPEC_OK;
+}
+
+int spec_kv_commit(void *kv, void *mirror, int elem_bytes, int L, int B, int H, int S, int D,
+                   const int32_t *cache_len, const int32_t *path_len, const int32_t *path_nodes,
+                   int N, int32_t *new_len, hipStream_t stream) {
+  if (!kv || !cache_len || !path_len || !new_len) return SPEC_ERR_NULL;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8)
+    return SPEC_ERR_PARAM;
+  if (L < 1 || B < 1 || H < 1 || S < 1 || D < 1 || N < 1 || N > kMaxN || N > S)
+    return SPEC_ERR_SHAPE;
+  const size_t row_bytes = (size_t)D * (size_t)elem_bytes;
+  if (row_bytes % 16 != 0) return SPEC_ERR_ALIGN;
+  if (!aligned(kv, 16) || (mirror && !aligned(mirror, 16))) return SPEC_ERR_ALIGN;
+  if (mirror == kv) return SPEC_ERR_PARAM;
+  // one head of a cycle (N rows) must fit a workgroup's registers
+  const long per_head = (long)N * (long)(row_bytes / 16);
+  if (per_head > sv::kv_items_per_wg()) return SPEC_ERR_SHAPE;
+  const int hb = (int)std::max(1L, std::min((long)H, (long)sv::kv_items_per_wg() / per_head));
+  const long groups = (long)L * 2 * B * ((H + hb - 1) / hb);
+  if (groups > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
+  if (sv::launch_kv_commit(kv, mirror, L, B, H, S, row_bytes, hb, cache_len, path_len,
+                           path_nodes, N, new_len, stream) != hipSuccess)
+    return SPEC_ERR_HIP;
   return SPEC_OK;
 }
 

@@ -123,3 +123,24 @@ def test_binding_requires_library(monkeypatch, tmp_path):
     monkeypatch.setattr(sv, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         sv.load()
+
+
+def _kv(**kw):
+    a = dict(kv=FAKE, mirror=None, es=2, L=2, B=3, H=2, S=80, D=128, cl=FAKE, pl=FAKE,
+             pn=FAKE, N=63, nl=FAKE, stream=None)
+    a.update(kw)
+    return sv.load().spec_kv_commit(a["kv"], a["mirror"], a["es"], a["L"], a["B"], a["H"],
+                                    a["S"], a["D"], a["cl"], a["pl"], a["pn"], a["N"], a["nl"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv=None), -1), (dict(cl=None), -1), (dict(pl=None), -1), (dict(nl=None), -1),
+    (dict(es=3), -3), (dict(es=0), -3), (dict(kv=FAKE, mirror=FAKE), -3),
+    (dict(L=0), -2), (dict(B=0), -2), (dict(H=0), -2), (dict(D=0), -2), (dict(N=0), -2),
+    (dict(N=65), -2), (dict(S=62), -2),
+    (dict(D=7), -5), (dict(kv=FAKE + 8), -5), (dict(mirror=FAKE + 4), -5),
+    (dict(D=1024, es=4), -2),  # one head of the cycle exceeds a workgroup's registers
+])
+def test_kv_commit_errors(kw, code):
+    assert _kv(**kw) == code
