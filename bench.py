@@ -84,7 +84,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--min-warmup-s", type=float, default=0.3,
                     help="keep warming up until this many seconds have passed")
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["kv"])
     ap.add_argument("--sets", type=int, default=3,
                     help="input sets rotated across steps (1 when one set is >= 512 MiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -93,6 +93,12 @@ def main():
                     help="only run a plain device copy of this many MiB, 20 times (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.workload == "kv":
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            sys.exit(2)
+        kv_bench(args)
+        return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
         return
@@ -234,6 +240,76 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def kv_bench(args):
+    """KV-cache commit after a cycle (spec_kv_commit): a Llama-3-8B-shaped
+    cache (32 layers, 8 KV heads of 128, bf16), B=32 requests with merged
+    trees of 63 nodes, accepted paths of random tree nodes, and a mirror (the
+    drafter's copy).  A step is one commit; it moves the same rows each time
+    (the cache contents change, the work does not)."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sample_amd as sv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.kv_commit_workload(seed=0)
+    L, _, B, H, S, D = w.kv.shape
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)
+                                    if a.dtype == np.uint16 else np.ascontiguousarray(a)).to(dev)
+    kv, mir = up(w.kv), up(w.mirror)
+    cl, pl, pn = up(w.cache_len), up(w.path_len), up(w.path_nodes)
+    new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    call = lambda: sv.kv_commit(kv, cl, pl, pn, mirror=mir, out=new_len)
+    call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t0 < args.min_warmup_s:
+        call()
+        i += 1
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    # algorithmic bytes: every path row read once, written where it moves,
+    # and written to the mirror
+    row = D * 2 * L * 2 * H
+    moved = sum(int((w.path_nodes[b, :w.path_len[b]] != np.arange(1, w.path_len[b] + 1)).sum())
+                for b in range(B))
+    rows_read = int((w.path_len + 1).sum())
+    algo = row * (rows_read + moved + rows_read)
+    achieved = algo / (ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.lib()
+        n, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_seconds:
+            oracle.kv_commit(w.kv, w.cache_len, w.path_len, w.path_nodes, mirror=w.mirror)
+            n += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": n * B / el, "unit": "requests/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} full commits of B={B} (whole-cache copies included), {el:.1f}s"}
+    print(json.dumps({
+        "metric": "KV-cache commit: requests/s and % peak HBM GB/s", "value": B / (ms * 1e-3),
+        "unit": "requests/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_steps_run": i, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"kv commit L{L} H{H} D{D} bf16 B{B} S{S} tree N{w.N} + mirror",
+                   "mean_path_len": float(w.path_len.mean()), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "k_kv_commit", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counters_for("kv", "k_kv_commit"), "kernel_us": ms * 1000.0,
+                     "kernel_us_from": "timed region / steps", "algorithmic_bytes": algo},
+        "cpu_baseline": cpu}), flush=True)
 
 
 def copy_probe(mib):

@@ -232,10 +232,9 @@ int spec_kv_commit(void *kv, void *mirror, int elem_bytes, int L, int B, int H, 
   // one head of a cycle (N rows) must fit a workgroup's registers
   const long per_head = (long)N * (long)(row_bytes / 16);
   if (per_head > sv::kv_items_per_wg()) return SPEC_ERR_SHAPE;
-  const int hb = (int)std::max(1L, std::min((long)H, (long)sv::kv_items_per_wg() / per_head));
-  const long groups = (long)L * 2 * B * ((H + hb - 1) / hb);
+  const long groups = (long)L * 2 * B;
   if (groups > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
-  if (sv::launch_kv_commit(kv, mirror, L, B, H, S, row_bytes, hb, cache_len, path_len,
+  if (sv::launch_kv_commit(kv, mirror, L, B, H, S, row_bytes, cache_len, path_len,
                            path_nodes, N, new_len, stream) != hipSuccess)
     return SPEC_ERR_HIP;
   return SPEC_OK;

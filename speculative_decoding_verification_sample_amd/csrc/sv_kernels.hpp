@@ -38,7 +38,7 @@ hipError_t launch_topp_select(const void *target, const void *draft, int dtype, 
 
 // KV-cache commit after a cycle (sv_kv.hip)
 hipError_t launch_kv_commit(void *kv, void *mirror, int L, int B, int H, int S, size_t row_bytes,
-                            int heads_per_wg, const int32_t *cache_len, const int32_t *path_len,
+                            const int32_t *cache_len, const int32_t *path_len,
                             const int32_t *path_nodes, int N, int32_t *new_len,
                             hipStream_t stream);
 // 16-byte pieces one commit workgroup holds at once
