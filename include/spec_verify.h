@@ -119,6 +119,27 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
                        float *out_p_draft, float *out_q_draft, float *out_residual_mass,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Sampling verify with per-request temperature and top-p, greedy and
+ * sampling requests mixed in one batch (temperature 0 is the greedy rule:
+ * accept a draft only if it is the target's top choice; lotook.com
+ * explainer, FAQ; the sampling rule and its settings as in
+ * spec_verify_sample).
+ *   Arguments as spec_verify_sample, except: temperature [B] float32 on the
+ *   device (0 = greedy for that request, else > 0 and finite); top_p [B]
+ *   float32 on the device, each in (0, 1], or NULL for 1 everywhere.
+ *   A greedy request reads only its target rows (its draft rows, u_accept
+ *   and u_sample are ignored); its out_p_draft / out_q_draft /
+ *   out_residual_mass entries are 0.  A request whose temperature or top_p
+ *   is out of range gets out_accepted = -3 and out_tokens = -1.
+ *   Workspace: spec_verify_workspace_bytes(SPEC_OP_SAMPLE, ..., use_top_p)
+ *   with use_top_p nonzero when top_p is not NULL. */
+int spec_verify_mixed(const void *target_logits, const void *draft_logits, int dtype,
+                      const int32_t *draft_tokens, const float *u_accept,
+                      const float *u_sample, const float *temperature, const float *top_p,
+                      int B, int K, int V, int32_t *out_accepted, int32_t *out_tokens,
+                      float *out_p_draft, float *out_q_draft, float *out_residual_mass,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Greedy verify of B merged draft trees of N nodes each.
  *   target_logits [B, N, V]: row i = the target's next-token logits after
  *     the path root..i; parents [B, N] int32 (parents[0] = -1, 0 <= parents[i] < i);

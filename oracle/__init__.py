@@ -158,6 +158,38 @@ def tree_is_valid(parents, anc_mask) -> bool:
     return bool(rc)
 
 
+def verify_mixed(target, draft, tokens, u_accept, u_sample, temperature, top_p=None):
+    """Per-request parameters: each request is verified on its own with its
+    own temperature (0: the greedy rule on its target rows) and top_p (the
+    requests are independent).  A request with a temperature not finite or
+    < 0, or a top_p outside (0, 1], is marked accepted = -3, tokens -1.
+    Returns the verify_sample fields; p, q, S are 0 for greedy requests."""
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    temperature = np.asarray(temperature, np.float32)
+    top_p = np.ones(B, np.float32) if top_p is None else np.asarray(top_p, np.float32)
+    out = dict(accepted=np.empty(B, np.int32), tokens=np.empty((B, K + 1), np.int32),
+               p=np.zeros((B, K)), q=np.zeros((B, K)), S=np.zeros(B),
+               flags=np.zeros(B, np.int32))
+    for b in range(B):
+        T, P = float(temperature[b]), float(top_p[b])
+        if not (np.isfinite(T) and T >= 0.0) or not (0.0 < P <= 1.0):
+            out["accepted"][b] = -3
+            out["tokens"][b] = -1
+            continue
+        if T == 0.0:
+            r = verify_greedy(target[b:b + 1], tokens[b:b + 1])
+        else:
+            r = verify_sample(target[b:b + 1], draft[b:b + 1], tokens[b:b + 1],
+                              u_accept[b:b + 1], u_sample[b:b + 1], T, P)
+            for key in ("p", "q", "S", "flags"):
+                out[key][b] = r[key][0]
+        out["accepted"][b] = r["accepted"][0]
+        out["tokens"][b] = r["tokens"][0]
+    return out
+
+
 def kv_commit(kv, cache_len, path_len, path_nodes=None, N=None, mirror=None):
     """KV-cache commit (oracle.c, oracle_kv_commit).  kv [L, 2, B, H, S, D]
     (any dtype: bytes are copied); path_nodes [B, N] int32 or None (linear:

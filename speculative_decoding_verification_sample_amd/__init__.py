@@ -8,7 +8,7 @@ current HIP stream.  If the library has not been built the calls raise: there
 is no fallback implementation.
 
 Entry points (same names as the C ABI, minus the ``spec_`` prefix):
-``verify_greedy``, ``verify_sample``, ``verify_tree``, ``kv_commit``,
+``verify_greedy``, ``verify_sample``, ``verify_mixed``, ``verify_tree``, ``kv_commit``,
 ``verify_workspace_bytes``, ``status_string``, ``profile_begin``,
 ``profile_end``.
 """
@@ -28,7 +28,7 @@ ERRORS = {-1: "SPEC_ERR_NULL", -2: "SPEC_ERR_SHAPE", -3: "SPEC_ERR_PARAM",
           -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_ALIGN", -6: "SPEC_ERR_HIP"}
 
 EXPORTS = ("spec_verify_workspace_bytes", "spec_verify_greedy", "spec_verify_sample",
-           "spec_verify_tree", "spec_kv_commit", "spec_status_string", "spec_profile_begin",
+           "spec_verify_mixed", "spec_verify_tree", "spec_kv_commit", "spec_status_string", "spec_profile_begin",
            "spec_profile_end")
 
 _lib = None
@@ -57,6 +57,8 @@ def load() -> ctypes.CDLL:
     L.spec_verify_greedy.restype = I
     L.spec_verify_sample.argtypes = [P, P, I, P, P, P, F, F, I, I, I, P, P, P, P, P, P, Z, P]
     L.spec_verify_sample.restype = I
+    L.spec_verify_mixed.argtypes = [P, P, I, P, P, P, P, P, I, I, I, P, P, P, P, P, P, Z, P]
+    L.spec_verify_mixed.restype = I
     L.spec_verify_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, Z, P]
     L.spec_verify_tree.restype = I
     L.spec_kv_commit.argtypes = [P, P, I, I, I, I, I, I, P, P, P, I, P, P]
@@ -202,6 +204,45 @@ def verify_sample(target, draft, draft_tokens, u_accept, u_sample, temperature: 
         _ws_ptr(ws), _ws_avail(ws), _stream(dev, stream))
     if rc != SPEC_OK:
         raise SpecVerifyError(rc, "spec_verify_sample")
+    return out
+
+
+def verify_mixed(target, draft, draft_tokens, u_accept, u_sample, temperature, top_p=None, *,
+                 diagnostics: bool = True, workspace=None, stream=None,
+                 out=None) -> Dict[str, object]:
+    """Per-request temperature [B] (0 = greedy) and top_p [B] (or None),
+    float32 device tensors; otherwise as verify_sample."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _check(target, "target", (B, K1, V), device=dev)
+    _check(draft, "draft", (B, K, V), target.dtype, dev)
+    _check(draft_tokens, "draft_tokens", (B, K), torch.int32, dev)
+    _check(u_accept, "u_accept", (B, K), torch.float32, dev)
+    _check(u_sample, "u_sample", (B,), torch.float32, dev)
+    _check(temperature, "temperature", (B,), torch.float32, dev)
+    if top_p is not None:
+        _check(top_p, "top_p", (B,), torch.float32, dev)
+    dt = _logit_dtype(target)
+    ws = _workspace(verify_workspace_bytes(SPEC_OP_SAMPLE, B, K, V, dt, top_p is not None), dev,
+                    workspace)
+    if out is None:
+        out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                   tokens=torch.empty((B, K1), dtype=torch.int32, device=dev))
+        if diagnostics:
+            out["p"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+            out["q"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+            out["residual_mass"] = torch.empty(B, dtype=torch.float32, device=dev)
+    _check(out["accepted"], "out accepted", (B,), torch.int32, dev)
+    _check(out["tokens"], "out tokens", (B, K1), torch.int32, dev)
+    rc = load().spec_verify_mixed(
+        _ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(u_accept), _ptr(u_sample),
+        _ptr(temperature), _ptr(top_p), B, K, V, _ptr(out["accepted"]), _ptr(out["tokens"]),
+        _ptr(out.get("p")), _ptr(out.get("q")), _ptr(out.get("residual_mass")),
+        _ws_ptr(ws), _ws_avail(ws), _stream(dev, stream))
+    if rc != SPEC_OK:
+        raise SpecVerifyError(rc, "spec_verify_mixed")
     return out
 
 

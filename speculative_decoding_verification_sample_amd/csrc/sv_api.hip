@@ -23,19 +23,6 @@ constexpr int kMaxN = 64;
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// log2(e) / T split into float hi + lo with lo > 0 (lo carries the rounding
-// of hi, so the product (l - m) * k keeps ~1 ulp accuracy per element).
-Scale make_scale(double k64) {
-  float hi = (float)k64;
-  if ((double)hi >= k64) hi = std::nextafter(hi, 0.0f);
-  float lo = (float)(k64 - (double)hi);
-  if (!(lo > 0.0f)) {
-    hi = std::nextafter(hi, 0.0f);
-    lo = (float)(k64 - (double)hi);
-  }
-  return Scale{hi, lo};
-}
-
 int check_shape(long B, long KN, long V, int op) {
   if (B < 1 || V < 1 || V > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
   if (op == SPEC_OP_TREE) {
@@ -142,55 +129,114 @@ int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draf
   return SPEC_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The sampling call with batch-wide (temps == NULL) or per-request
+// parameters; arguments already validated except the workspace.
+int run_sample(const void *target_logits, const void *draft_logits, int dtype,
+               const int32_t *draft_tokens, const float *u_accept, const float *u_sample,
+               double k64, float top_p, const float *temps, const float *topps, int B, int K,
+               int V, int32_t *out_accepted, int32_t *out_tokens, float *out_p_draft,
+               float *out_q_draft, float *out_residual_mass, void *workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  const bool use_top_p = topps != nullptr || top_p < 1.0f;
+  const Layout L = sv::make_layout(SPEC_OP_SAMPLE, B, K, V, dtype, use_top_p);
+  int rc;
+  if ((rc = check_workspace(workspace, workspace_bytes, L))) return rc;
+  sv::SampleArgs a;
+  a.target = (const char *)target_logits;
+  a.draft = (const char *)draft_logits;
+  a.tokens = draft_tokens;
+  a.u_accept = u_accept;
+  a.u_sample = u_sample;
+  a.temps = temps;
+  a.topps = topps;
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.S = L.S;
+  a.SB = L.SB;
+  a.k64 = k64;
+  a.top_p = (double)top_p;
+  a.k = sv::make_scale(k64);
+  a.epoch = next_epoch();
+  a.part_m = carve<sv::u64>(workspace, L.part_m);
+  a.part_z = carve<sv::u64>(workspace, L.part_z);
+  a.part_x = carve<sv::u64>(workspace, L.part_x);
+  a.rowstat = use_top_p ? carve<sv::RowStat>(workspace, L.rowstat) : nullptr;
+  a.rtot = carve<sv::u64>(workspace, L.rtot);
+  a.rent = carve<sv::u64>(workspace, L.rent);
+  a.out_accepted = out_accepted;
+  a.out_tokens = out_tokens;
+  a.out_p = out_p_draft;
+  a.out_q = out_q_draft;
+  a.out_mass = out_residual_mass;
+  // residual tiles trail their request's streaming tiles by about one
+  // resident wave of requests
+  a.lag = sv::resident_workgroups(dtype) / ((2 * K + 1) * L.S) + 1;
+  a.phase = use_top_p ? 1 : 0;
+  prof_before(stream);
+  if (sv::launch_sample(a, dtype, stream) != hipSuccess) return SPEC_ERR_HIP;
+  prof_after(stream);
+  if (use_top_p) {
+    if (sv::launch_topp_select(a, dtype, stream) != hipSuccess) return SPEC_ERR_HIP;
+    a.phase = 2;
+    if (sv::launch_sample(a, dtype, stream) != hipSuccess) return SPEC_ERR_HIP;
+  }
+  return SPEC_OK;
+}
+
+int check_sample_args(const void *target_logits, const void *draft_logits, int dtype,
+                      const int32_t *draft_tokens, const float *u_accept, const float *u_sample,
+                      int B, int K, int V, int32_t *out_accepted, int32_t *out_tokens) {
+  if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_sample ||
+      !out_accepted || !out_tokens)
+    return SPEC_ERR_NULL;
+  if (!dtype_ok(dtype)) return SPEC_ERR_PARAM;
+  int rc = check_shape(B, K, V, SPEC_OP_SAMPLE);
+  if (rc) return rc;
+  if (!aligned(target_logits, sv::elem_bytes(dtype)) || !aligned(draft_logits, sv::elem_bytes(dtype)))
+    return SPEC_ERR_ALIGN;
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int spec_verify_sample(const void *target_logits, const void *draft_logits, int dtype,
                        const int32_t *draft_tokens, const float *u_accept,
                        const float *u_sample, float temperature, float top_p, int B, int K,
                        int V, int32_t *out_accepted, int32_t *out_tokens, float *out_p_draft,
                        float *out_q_draft, float *out_residual_mass, void *workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-  if (!target_logits || !draft_logits || !draft_tokens || !u_accept || !u_sample ||
-      !out_accepted || !out_tokens)
-    return SPEC_ERR_NULL;
-  if (!dtype_ok(dtype)) return SPEC_ERR_PARAM;
+  int rc = check_sample_args(target_logits, draft_logits, dtype, draft_tokens, u_accept,
+                             u_sample, B, K, V, out_accepted, out_tokens);
+  if (rc) return rc;
   if (!std::isfinite(temperature) || !(temperature > 0.0f)) return SPEC_ERR_PARAM;
   if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return SPEC_ERR_PARAM;
-  int rc = check_shape(B, K, V, SPEC_OP_SAMPLE);
-  if (rc) return rc;
-  if (!aligned(target_logits, sv::elem_bytes(dtype)) || !aligned(draft_logits, sv::elem_bytes(dtype)))
-    return SPEC_ERR_ALIGN;
-  const double k64 = 1.4426950408889634 / (double)temperature;  // log2(e) / T
+  const double k64 = sv::kLog2e / (double)temperature;  // log2(e) / T
   if (!std::isfinite(k64) || !(k64 > 0.0) || k64 > 3.0e38) return SPEC_ERR_PARAM;
-  const int use_top_p = top_p < 1.0f;
-  const Layout L = sv::make_layout(SPEC_OP_SAMPLE, B, K, V, dtype, use_top_p);
-  if ((rc = check_workspace(workspace, workspace_bytes, L))) return rc;
-  const Scale k = make_scale(k64);
-  sv::u64 *part_m = carve<sv::u64>(workspace, L.part_m);
-  sv::u64 *part_z = carve<sv::u64>(workspace, L.part_z);
-  sv::u64 *part_x = carve<sv::u64>(workspace, L.part_x);
-  sv::RowStat *rowstat = use_top_p ? carve<sv::RowStat>(workspace, L.rowstat) : nullptr;
-  sv::u64 *rtot = carve<sv::u64>(workspace, L.rtot);
-  sv::u64 *rent = carve<sv::u64>(workspace, L.rent);
-  const int rows_t = B * (K + 1), rows_d = B * K;
-  const sv::u64 epoch = next_epoch();
-  // residual tiles trail their request's streaming tiles by about one
-  // resident wave of requests
-  const int lag = sv::resident_workgroups(dtype) / ((2 * K + 1) * L.S) + 1;
-  auto run = [&](int phase) {
-    return sv::launch_sample(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample,
-                             B, K, V, L.S, L.SB, k64, k, epoch, phase, lag, part_m, part_z, part_x, rowstat,
-                             rtot, rent, out_accepted, out_tokens, out_p_draft,
-                             out_q_draft, out_residual_mass, stream);
-  };
-  prof_before(stream);
-  if (run(use_top_p ? 1 : 0) != hipSuccess) return SPEC_ERR_HIP;
-  prof_after(stream);
-  if (use_top_p) {
-    if (sv::launch_topp_select(target_logits, draft_logits, dtype, rows_t, rows_d, V, L.S, k, k64,
-                               (double)top_p, part_m, part_z, rowstat, stream) != hipSuccess)
-      return SPEC_ERR_HIP;
-    if (run(2) != hipSuccess) return SPEC_ERR_HIP;
-  }
-  return SPEC_OK;
+  return run_sample(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample, k64,
+                    top_p, nullptr, nullptr, B, K, V, out_accepted, out_tokens, out_p_draft,
+                    out_q_draft, out_residual_mass, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_mixed(const void *target_logits, const void *draft_logits, int dtype,
+                      const int32_t *draft_tokens, const float *u_accept, const float *u_sample,
+                      const float *temperature, const float *top_p, int B, int K, int V,
+                      int32_t *out_accepted, int32_t *out_tokens, float *out_p_draft,
+                      float *out_q_draft, float *out_residual_mass, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_sample_args(target_logits, draft_logits, dtype, draft_tokens, u_accept,
+                             u_sample, B, K, V, out_accepted, out_tokens);
+  if (rc) return rc;
+  if (!temperature) return SPEC_ERR_NULL;
+  return run_sample(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample, 1.0,
+                    1.0f, temperature, top_p, B, K, V, out_accepted, out_tokens, out_p_draft,
+                    out_q_draft, out_residual_mass, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parents,

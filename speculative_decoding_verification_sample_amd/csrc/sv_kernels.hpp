@@ -19,22 +19,13 @@ hipError_t launch_tree(const void *target, int dtype, const int32_t *parents,
 
 // sampling verify (sv_sample.hip); phase 0 = whole call in one kernel,
 // 1 = streaming tiles only, 2 = residual tiles only (around the top-p kernel)
-hipError_t launch_sample(const void *target, const void *draft, int dtype, const int32_t *tokens,
-                         const float *u_accept, const float *u_sample, int B, int K, int V,
-                         int S, int SB, double k64, Scale k, u64 epoch, int phase, int lag,
-                         u64 *part_m, u64 *part_z, u64 *part_x, const RowStat *rowstat,
-                         u64 *rtot, u64 *rent, int32_t *out_accepted,
-                         int32_t *out_tokens, float *out_p, float *out_q, float *out_mass,
-                         hipStream_t stream);
+hipError_t launch_sample(const SampleArgs &args, int dtype, hipStream_t stream);
 
 // workgroups of the fused sampling kernel resident at once (cached per dtype)
 int resident_workgroups(int dtype);
 
 // top-p nucleus threshold per row (sv_topp.hip)
-hipError_t launch_topp_select(const void *target, const void *draft, int dtype, int rows_t,
-                              int rows_d, int V, int S, Scale k, double k64, double top_p,
-                              const u64 *part_m, const u64 *part_z, RowStat *rowstat,
-                              hipStream_t stream);
+hipError_t launch_topp_select(const SampleArgs &args, int dtype, hipStream_t stream);
 
 // KV-cache commit after a cycle (sv_kv.hip)
 hipError_t launch_kv_commit(void *kv, void *mirror, int L, int B, int H, int S, size_t row_bytes,

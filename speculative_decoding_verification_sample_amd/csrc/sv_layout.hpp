@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <math.h>
 
 namespace sv {
 
@@ -40,6 +41,21 @@ struct Scale {
   float hi, lo;
 };
 
+// k = log2(e) / T split into float hi + lo with lo > 0 (lo carries the
+// rounding of hi, so the product (l - m) * k keeps ~1 ulp accuracy per
+// element).  The same steps on the host and on the device.
+__host__ __device__ inline Scale make_scale(double k64) {
+  float hi = (float)k64;
+  if ((double)hi >= k64) hi = nextafterf(hi, 0.0f);
+  float lo = (float)(k64 - (double)hi);
+  if (!(lo > 0.0f)) {
+    hi = nextafterf(hi, 0.0f);
+    lo = (float)(k64 - (double)hi);
+  }
+  return Scale{hi, lo};
+}
+constexpr double kLog2e = 1.4426950408889634;
+
 // One row's softmax statistics after combining its splits (and top-p).
 struct RowStat {
   double z;   // sum over the row of 2^((l - m) k)
@@ -70,6 +86,62 @@ constexpr int kModeBonus = 1;
 constexpr int kEntriesB = kThreads + 2;
 // Largest number of residual splits per row (the draw stages them in LDS).
 constexpr int kMaxSplitsB = 512;
+
+// Arguments of the fused sampling kernel (and what a call shares with the
+// top-p kernel).  temps / topps: per-request temperature and top-p on the
+// device (NULL: the batch-wide k, k64, top_p apply).
+struct SampleArgs {
+  const char *target, *draft;
+  const int32_t *tokens;
+  const float *u_accept, *u_sample;
+  const float *temps, *topps;
+  int B, K, V, S, SB;
+  double k64, top_p;
+  Scale k;
+  u64 epoch;
+  int phase, lag;
+  u64 *part_m, *part_z, *part_x;
+  RowStat *rowstat;
+  u64 *rtot, *rent;
+  int32_t *out_accepted, *out_tokens;
+  float *out_p, *out_q, *out_mass;
+};
+
+// A request's sampling parameters, as the kernels see them.
+struct ReqParams {
+  bool invalid;  // temperature not finite or < 0, or top_p not in (0, 1]
+  bool greedy;   // temperature 0
+  double k64, top_p;
+  Scale k;
+};
+
+__host__ __device__ inline ReqParams request_params(const float *temps, const float *topps,
+                                                    double k64, Scale k, double top_p, int b) {
+  ReqParams q;
+  q.invalid = false;
+  q.greedy = false;
+  q.k64 = k64;
+  q.k = k;
+  q.top_p = top_p;
+  if (temps) {
+    const float T = temps[b];
+    if (!(T >= 0.0f) || !(T < INFINITY)) {
+      q.invalid = true;
+    } else if (T == 0.0f) {
+      q.greedy = true;
+    } else {
+      q.k64 = kLog2e / (double)T;
+      if (!(q.k64 <= 3.0e38)) q.invalid = true;
+      else q.k = make_scale(q.k64);
+    }
+  }
+  if (topps) {
+    const float p = topps[b];
+    if (!(p > 0.0f) || !(p <= 1.0f)) q.invalid = true;
+    else q.top_p = (double)p;
+  }
+  return q;
+}
 
 struct Layout {
   int S = 0;       // streaming splits per row

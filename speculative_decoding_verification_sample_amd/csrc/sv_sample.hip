@@ -123,7 +123,7 @@ __device__ __forceinline__ bool read_cell(const u64 *part_m, const u64 *part_z, 
 
 // The accept / reject outcome of request b into *sd; whole workgroup.
 // Returns false if a partial never arrived (bounded wait timed out).
-__device__ bool decide(const int32_t *tokens, const float *u_accept, int B, int K, int S,
+__device__ __forceinline__ bool decide(const int32_t *tokens, const float *u_accept, int B, int K, int S,
                        double k64, Scale k, const u64 *part_m, const u64 *part_z,
                        const u64 *part_x, u64 epoch,
                        const RowStat *rowstat, int b, bool write_outputs, int32_t *out_accepted,
@@ -382,7 +382,7 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
 // the split-relative token in every thread; if rounding leaves no crossing,
 // the last token with positive mass.  Whole workgroup.
 template <int DT, bool TOPP, bool P>
-__device__ int draw_split(const SplitGeo &g, double e_head, double e_lane, double e_tail,
+__device__ __forceinline__ int draw_split(const SplitGeo &g, double e_head, double e_lane, double e_tail,
                           double rem, const Decision &d, Scale k, DrawLds &D) {
   __shared__ int s_ent;
   __shared__ double s_base;
@@ -451,7 +451,7 @@ __device__ int draw_split(const SplitGeo &g, double e_head, double e_lane, doubl
 }
 
 template <int DT, bool TOPP>
-__device__ void residual_tile(const char *target, const char *draft, const int32_t *tokens,
+__device__ __forceinline__ void residual_tile(const char *target, const char *draft, const int32_t *tokens,
                               const float *u_accept, const float *u_sample, int B, int K, int V,
                               int S, int SB, double k64, Scale k, u64 epoch,
                               const u64 *part_m, const u64 *part_z, const u64 *part_x,
@@ -618,32 +618,106 @@ __device__ void residual_tile(const char *target, const char *draft, const int32
   }
 }
 
+// A greedy request inside a sampling call (temperature 0): the residual
+// tile 0 combines the argmax keys of target rows 0..K with its first wave,
+// accepts drafts while each equals the top choice, and emits the top choice
+// at the first mismatch (lotook.com explainer, FAQ: at temperature 0 a draft
+// is accepted only if it is the target's top choice).
+__device__ __forceinline__ void greedy_in_sample(const SampleArgs &a, int b) {
+  const int i = threadIdx.x;  // < 64
+  const int K = a.K, S = a.S;
+  int am = -1, x = -1;
+  bool ok = true;
+  if (i <= K) {
+    const size_t g0 = ((size_t)b * (K + 1) + i) * S;
+    u64 best = 0;
+    for (int s = 0; s < S && ok; ++s) {
+      bool got = false;
+      for (int it = 0; it < kSpinLimit && !got; ++it) {
+        uint32_t hi, lo;
+        got = ((int)unpack_u32(load_agent(&a.part_m[g0 + s]), a.epoch, &hi) &
+               (int)unpack_u32(load_agent(&a.part_z[g0 + s]), a.epoch, &lo)) != 0;
+        if (got) {
+          const u64 key = ((u64)hi << 32) | lo;
+          best = key > best ? key : best;
+        } else {
+          spin_pause();
+        }
+      }
+      ok = got;
+    }
+    am = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
+  }
+  if (i < K) x = a.tokens[(size_t)b * K + i];
+  if (__ballot(!ok)) {
+    if (i == 0) a.out_accepted[b] = -2;  // time-out: flag the request as failed
+    return;
+  }
+  const uint64_t miss = __ballot(i < K && x != am);
+  const int n = miss ? __builtin_ctzll(miss) : K;
+  if (i <= K) a.out_tokens[(size_t)b * (K + 1) + i] = i < n ? x : (i == n ? am : -1);
+  if (i < K) {
+    if (a.out_p) a.out_p[(size_t)b * K + i] = 0.f;
+    if (a.out_q) a.out_q[(size_t)b * K + i] = 0.f;
+  }
+  if (i == 0) {
+    a.out_accepted[b] = n;
+    if (a.out_mass) a.out_mass[b] = 0.f;
+  }
+}
+
 }  // namespace
 
-template <int DT>
+// The pointers come in as separate restrict-qualified arguments: the
+// compiler may then take the uniform reads (the draft tokens above all) as
+// scalar loads that do not hold up the stream's vector loads.
+// MIXED: per-request parameters (temps / topps on the device); otherwise the
+// batch-wide ones and no greedy requests (the per-request code stays out of
+// the batch-wide kernel, where it would cost registers and issue slots).
+template <int DT, bool MIXED>
 __global__ __launch_bounds__(kThreads) void k_sample_fused(
     const char *__restrict__ target, const char *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
-    const float *__restrict__ u_sample, int B, int K, int V, int S, int SB, double k64, Scale k,
-    u64 epoch, int phase, int lag, u64 *__restrict__ part_m, u64 *__restrict__ part_z,
-    u64 *__restrict__ part_x, const RowStat *__restrict__ rowstat, u64 *__restrict__ rtot,
-    u64 *__restrict__ rent,
-    int32_t *__restrict__ out_accepted, int32_t *__restrict__ out_tokens,
-    float *__restrict__ out_p, float *__restrict__ out_q, float *__restrict__ out_mass) {
+    const float *__restrict__ u_sample, const float *__restrict__ temps,
+    const float *__restrict__ topps, u64 *__restrict__ part_m, u64 *__restrict__ part_z,
+    u64 *__restrict__ part_x, RowStat *__restrict__ rowstat, u64 *__restrict__ rtot,
+    u64 *__restrict__ rent, int32_t *__restrict__ out_accepted,
+    int32_t *__restrict__ out_tokens, float *__restrict__ out_p, float *__restrict__ out_q,
+    float *__restrict__ out_mass, SampleArgs a) {
+  a.target = target;
+  a.draft = draft;
+  a.tokens = tokens;
+  a.u_accept = u_accept;
+  a.u_sample = u_sample;
+  a.temps = temps;
+  a.topps = topps;
+  a.part_m = part_m;
+  a.part_z = part_z;
+  a.part_x = part_x;
+  a.rowstat = rowstat;
+  a.rtot = rtot;
+  a.rent = rent;
+  a.out_accepted = out_accepted;
+  a.out_tokens = out_tokens;
+  a.out_p = out_p;
+  a.out_q = out_q;
+  a.out_mass = out_mass;
   const int blk = (int)blockIdx.x;
+  const int B = a.B, K = a.K, V = a.V, S = a.S, SB = a.SB;
   const int R = 2 * K + 1;
   const int nA_req = R * S;
   bool streaming;
   int b, idx;
-  if (phase == 1) {  // streaming tiles only
+  if (a.phase == 1) {  // streaming tiles only
     streaming = true;
     b = blk / nA_req;
     idx = blk - b * nA_req;
-  } else if (phase == 2) {  // residual tiles only
+  } else if (a.phase == 2) {  // residual tiles only
     streaming = false;
     b = blk / SB;
     idx = blk - b * SB;
   } else {  // group g holds [streaming(g) | residual(g - lag)]
+    const int lag = a.lag;
     auto prefix = [&](int g) { return nA_req * min(g, B) + SB * min(max(g - lag, 0), B); };
     int lo = 0, hi = B + lag;
     while (hi - lo > 1) {
@@ -656,32 +730,56 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     b = streaming ? lo : lo - lag;
     idx = streaming ? off : off - a_here;
   }
+  ReqParams q;
+  if (MIXED) {
+    q = request_params(a.temps, a.topps, a.k64, a.k, a.top_p, b);
+  } else {
+    q.invalid = false;
+    q.greedy = false;
+    q.k64 = a.k64;
+    q.k = a.k;
+    q.top_p = a.top_p;
+  }
+  if (q.invalid) {  // a request's own parameters are out of range
+    if (!streaming && idx == 0 && threadIdx.x <= K) {
+      a.out_tokens[(size_t)b * (K + 1) + threadIdx.x] = -1;
+      if (threadIdx.x == 0) a.out_accepted[b] = -3;
+    }
+    return;
+  }
   if (streaming) {
     const int r = idx / S;
     const int s = idx - r * S;
     const int rows_t = B * (K + 1);
     const int grow = r <= K ? b * (K + 1) + r : rows_t + b * K + (r - K - 1);
-    const char *rp = r <= K ? row_ptr(target, (size_t)grow, V, DT)
-                            : row_ptr(draft, (size_t)(grow - rows_t), V, DT);
-    // the draft token's logit, if this split holds it (or, for a token out
-    // of range, split 0 publishes -inf: probability 0, the draft is rejected)
-    // (uniform across the workgroup: scalar registers, no vector registers
-    // held across the stream)
+    if (q.greedy) {  // top choices of the target rows; the draft rows are not read
+      if (r > K) return;
+      const uint64_t key = argmax_tile<DT>(row_ptr(a.target, (size_t)grow, V, DT), V, s);
+      if (threadIdx.x == 0) {
+        store_agent(&a.part_m[(size_t)grow * S + s], pack_u32((uint32_t)(key >> 32), a.epoch));
+        store_agent(&a.part_z[(size_t)grow * S + s], pack_u32((uint32_t)key, a.epoch));
+      }
+      return;
+    }
+    const char *rp = r <= K ? row_ptr(a.target, (size_t)grow, V, DT)
+                            : row_ptr(a.draft, (size_t)(grow - rows_t), V, DT);
+    // the draft token's logit, if this split holds it (for a token out of
+    // range split 0 publishes -inf: probability 0, the draft is rejected).
+    // Everything here is uniform across the workgroup, so it lives in scalar
+    // registers: the logits are read-only for the whole call, and the aligned
+    // dword holding the element (same page, so always readable) comes with a
+    // scalar load through the constant address space, leaving the vector
+    // queue to the stream; its bits are picked apart after the stream.
     const int pos = r <= K ? r : r - K - 1;  // position; target row K has no draft token
     bool mine = false, valid = false;
     unsigned mis = 0;
     uint32_t w = 0;
     if (r != K) {
-      const int x = tokens[(size_t)b * K + pos];
+      const int x = a.tokens[(size_t)b * K + pos];
       const int e0 = s * split_elems(DT), e1 = min(V, e0 + split_elems(DT));
       valid = x >= 0 && x < V;
       mine = (valid && x >= e0 && x < e1) || (!valid && s == 0);
       if (mine && valid) {
-        // the aligned dword holding the element (same page, so always
-        // readable); its bits are picked apart only after the stream
-        // the logits are read-only for the whole call: a scalar load through
-        // the constant address space, which leaves the vector queue to the
-        // stream
         typedef const __attribute__((address_space(4))) uint32_t *const_u32p;
         const uintptr_t ea = reinterpret_cast<uintptr_t>(rp) + (uintptr_t)x * elem_bytes(DT);
         mis = (unsigned)(ea & 3u);
@@ -690,51 +788,50 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     }
     float M;
     double Z;
-    softmax_tile<DT>(rp, V, s, k, &M, &Z);
+    softmax_tile<DT>(rp, V, s, q.k, &M, &Z);
     if (threadIdx.x == 0) {
-      store_agent(&part_m[(size_t)grow * S + s], pack_f32(M, epoch));
-      store_agent(&part_z[(size_t)grow * S + s], pack_f64(Z, epoch));
+      store_agent(&a.part_m[(size_t)grow * S + s], pack_f32(M, a.epoch));
+      store_agent(&a.part_z[(size_t)grow * S + s], pack_f64(Z, a.epoch));
       if (mine) {
         const uint32_t lx_bits = !valid ? 0xFF800000u  // -inf
                                  : DT == kBF16 ? (mis ? (w & 0xFFFF0000u) : (w << 16)) : w;
-        store_agent(part_x + ((size_t)b * K + pos) * 2 + (r <= K ? 0 : 1),
-                    pack_u32(lx_bits, epoch));
+        store_agent(a.part_x + ((size_t)b * K + pos) * 2 + (r <= K ? 0 : 1),
+                    pack_u32(lx_bits, a.epoch));
       }
     }
     return;
   }
+  if (q.greedy) {
+    if (idx == 0 && threadIdx.x < 64) greedy_in_sample(a, b);
+    return;
+  }
   __shared__ ResidLds rl;
-  if (rowstat)
-    residual_tile<DT, true>(target, draft, tokens, u_accept, u_sample, B, K, V, S, SB, k64, k,
-                            epoch, part_m, part_z, part_x, rowstat, rtot, rent, out_accepted,
-                            out_tokens, out_p, out_q, out_mass, b, idx, rl);
+  if (a.rowstat)
+    residual_tile<DT, true>(a.target, a.draft, a.tokens, a.u_accept, a.u_sample, B, K, V, S, SB,
+                            q.k64, q.k, a.epoch, a.part_m, a.part_z, a.part_x, a.rowstat,
+                            a.rtot, a.rent, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
+                            a.out_mass, b, idx, rl);
   else
-    residual_tile<DT, false>(target, draft, tokens, u_accept, u_sample, B, K, V, S, SB, k64, k,
-                             epoch, part_m, part_z, part_x, rowstat, rtot, rent, out_accepted,
-                             out_tokens, out_p, out_q, out_mass, b, idx, rl);
+    residual_tile<DT, false>(a.target, a.draft, a.tokens, a.u_accept, a.u_sample, B, K, V, S,
+                             SB, q.k64, q.k, a.epoch, a.part_m, a.part_z, a.part_x, a.rowstat,
+                             a.rtot, a.rent, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
+                             a.out_mass, b, idx, rl);
 }
 
-hipError_t launch_sample(const void *target, const void *draft, int dtype, const int32_t *tokens,
-                         const float *u_accept, const float *u_sample, int B, int K, int V,
-                         int S, int SB, double k64, Scale k, u64 epoch, int phase, int lag,
-                         u64 *part_m, u64 *part_z, u64 *part_x, const RowStat *rowstat,
-                         u64 *rtot, u64 *rent, int32_t *out_accepted, int32_t *out_tokens,
-                         float *out_p, float *out_q, float *out_mass, hipStream_t stream) {
-  const int nA = B * (2 * K + 1) * S;
-  const int nB = B * SB;
+hipError_t launch_sample(const SampleArgs &args, int dtype, hipStream_t stream) {
+  SampleArgs a = args;
+  const int nA = a.B * (2 * a.K + 1) * a.S;
+  const int nB = a.B * a.SB;
   // phase: 0 = whole call, 1 = streaming tiles only, 2 = residual tiles only
-  const int blocks = phase == 0 ? nA + nB : phase == 1 ? nA : nB;
-  lag = std::max(1, std::min(lag, B));
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(k_sample_fused<kBF16>, dim3(blocks), dim3(kThreads), 0, stream,
-                       (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
-                       K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, part_x, rowstat,
-                       rtot, rent, out_accepted, out_tokens, out_p, out_q, out_mass);
-  else
-    hipLaunchKernelGGL(k_sample_fused<kF32>, dim3(blocks), dim3(kThreads), 0, stream,
-                       (const char *)target, (const char *)draft, tokens, u_accept, u_sample, B,
-                       K, V, S, SB, k64, k, epoch, phase, lag, part_m, part_z, part_x, rowstat,
-                       rtot, rent, out_accepted, out_tokens, out_p, out_q, out_mass);
+  const int blocks = a.phase == 0 ? nA + nB : a.phase == 1 ? nA : nB;
+  a.lag = std::max(1, std::min(a.lag, a.B));
+  const bool mixed = a.temps != nullptr || a.topps != nullptr;
+  auto kern = dtype == kBF16 ? (mixed ? k_sample_fused<kBF16, true> : k_sample_fused<kBF16, false>)
+                             : (mixed ? k_sample_fused<kF32, true> : k_sample_fused<kF32, false>);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, stream, a.target, a.draft, a.tokens,
+                     a.u_accept, a.u_sample, a.temps, a.topps, a.part_m, a.part_z, a.part_x,
+                     a.rowstat, a.rtot, a.rent, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
+                     a.out_mass, a);
   return hipGetLastError();
 }
 
@@ -747,7 +844,8 @@ int resident_workgroups(int dtype) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 2048;
-    const void *fn = d ? (const void *)k_sample_fused<kBF16> : (const void *)k_sample_fused<kF32>;
+    const void *fn = d ? (const void *)k_sample_fused<kBF16, false>
+                       : (const void *)k_sample_fused<kF32, false>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess)
       per_cu = 4;
     cache[d] = std::max(1, cus * per_cu);

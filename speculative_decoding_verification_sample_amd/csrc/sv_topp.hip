@@ -70,16 +70,22 @@ __device__ __forceinline__ void for_row(const char *row, int V, F &&f) {
 }  // namespace
 
 template <int DT>
-__global__ __launch_bounds__(kTopThreads) void k_topp_select(
-    const char *__restrict__ target, const char *__restrict__ draft, int rows_t, int V, int S,
-    Scale k, double k64, double top_p, const u64 *__restrict__ part_m,
-    const u64 *__restrict__ part_z, RowStat *__restrict__ rowstat) {
+__global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int w = t >> 6;
+  const int V = a.V, S = a.S;
+  const int rows_t = a.B * (a.K + 1);
   const size_t row_bytes = (size_t)V * elem_bytes(DT);
-  const char *rp = row < rows_t ? target + (size_t)row * row_bytes
-                                : draft + (size_t)(row - rows_t) * row_bytes;
+  const char *rp = row < rows_t ? a.target + (size_t)row * row_bytes
+                                : a.draft + (size_t)(row - rows_t) * row_bytes;
+  const int b = row < rows_t ? row / (a.K + 1) : (row - rows_t) / a.K;
+  const ReqParams q = request_params(a.temps, a.topps, a.k64, a.k, a.top_p, b);
+  if (q.invalid || q.greedy) return;  // no softmax statistics for this request
+  const Scale k = q.k;
+  const double k64 = q.k64, top_p = q.top_p;
+  const u64 *part_m = a.part_m, *part_z = a.part_z;
+  RowStat *rowstat = a.rowstat;
 
   __shared__ double hist[kTopWaves][kBins];
   __shared__ double mass[kBins];
@@ -117,6 +123,17 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(
   __syncthreads();
   const float M = sM;
   const double Z = sZ;
+  if (!(top_p < 1.0)) {  // no nucleus for this request: everything is kept
+    if (t == 0) {
+      RowStat rs;
+      rs.m = M;
+      rs.z = Z;
+      rs.tau = -INFINITY;
+      rs.zk = Z;
+      rowstat[row] = rs;
+    }
+    return;
+  }
   const double goal = top_p * Z;
   const float kr = (k.hi + k.lo) * kBinsPerLog2;
 
@@ -258,19 +275,12 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(
   }
 }
 
-hipError_t launch_topp_select(const void *target, const void *draft, int dtype, int rows_t,
-                              int rows_d, int V, int S, Scale k, double k64, double top_p,
-                              const u64 *part_m, const u64 *part_z, RowStat *rowstat,
-                              hipStream_t stream) {
-  dim3 grid(rows_t + rows_d), block(kTopThreads);
+hipError_t launch_topp_select(const SampleArgs &a, int dtype, hipStream_t stream) {
+  dim3 grid(a.B * (2 * a.K + 1)), block(kTopThreads);
   if (dtype == kBF16)
-    hipLaunchKernelGGL(k_topp_select<kBF16>, grid, block, 0, stream, (const char *)target,
-                       (const char *)draft, rows_t, V, S, k, k64, top_p, part_m, part_z,
-                       rowstat);
+    hipLaunchKernelGGL(k_topp_select<kBF16>, grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(k_topp_select<kF32>, grid, block, 0, stream, (const char *)target,
-                       (const char *)draft, rows_t, V, S, k, k64, top_p, part_m, part_z,
-                       rowstat);
+    hipLaunchKernelGGL(k_topp_select<kF32>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -144,3 +144,13 @@ def _kv(**kw):
 ])
 def test_kv_commit_errors(kw, code):
     assert _kv(**kw) == code
+
+
+def test_mixed_errors():
+    L = sv.load()
+    call = lambda **kw: L.spec_verify_mixed(
+        kw.get("t", FAKE), FAKE, 0, FAKE, FAKE, FAKE, kw.get("temps", FAKE), None, 2, 3, 100,
+        FAKE, FAKE, None, None, None, FAKE, kw.get("wsb", 1 << 30), None)
+    assert call(temps=None) == -1
+    assert call(t=None) == -1
+    assert call(wsb=0) == -4
