@@ -33,7 +33,10 @@ if ROOT not in sys.path:
 METRIC = "verified logit-positions/s and % peak HBM GB/s at B=64 K=8 V=128256 bf16"
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 MALL_BYTES = 256 << 20  # MI355X memory-side (Infinity) cache
-WORKLOADS = {"c1": 0, "c2": 1, "c3": 2, "c4": 3, "c5": 4}
+WORKLOADS = {"c1": 0, "c2": 1, "c3": 2, "c4": 3, "c5": 4, "mixed": 2}
+# the mixed batch: the headline inputs, one request in four greedy, the others
+# at temperatures 0.7, 1.0, 0.5 in turn (spec_verify_mixed)
+MIXED_TEMPS = (0.0, 0.7, 1.0, 0.5)
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
@@ -84,7 +87,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--min-warmup-s", type=float, default=0.3,
                     help="keep warming up until this many seconds have passed")
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["kv"])
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["kv"],
+                    help="c1..c5: the five settings; mixed: the headline inputs with "
+                         "per-request temperatures; kv: the KV-cache commit")
     ap.add_argument("--sets", type=int, default=3,
                     help="input sets rotated across steps (1 when one set is >= 512 MiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -139,7 +144,14 @@ def main():
     ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
     calls = []
     for w in sets:
-        if w.kind == "sample":
+        if args.workload == "mixed":
+            a = (up(w.target), up(w.draft), up(w.tokens), up(w.u_accept), up(w.u_sample))
+            temps = up(np.array([MIXED_TEMPS[b % 4] for b in range(w.B)], np.float32))
+            out = dict(accepted=torch.empty(w.B, dtype=torch.int32, device=dev),
+                       tokens=torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev))
+            calls.append(lambda a=a, temps=temps, out=out: sv.verify_mixed(
+                *a, temps, None, diagnostics=False, workspace=ws, out=out))
+        elif w.kind == "sample":
             a = (up(w.target), up(w.draft), up(w.tokens), up(w.u_accept), up(w.u_sample))
             out = dict(accepted=torch.empty(w.B, dtype=torch.int32, device=dev),
                        tokens=torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev))
@@ -208,6 +220,10 @@ def main():
     positions = w0.positions
     value = positions / (ms_per_step / 1000.0)
     algo_bytes = w0.logit_bytes  # every logit read once
+    if args.workload == "mixed":  # a greedy request reads only its target rows
+        row = w0.V * (2 if w0.dtype == "bf16" else 4)
+        n_greedy = sum(1 for b in range(w0.B) if MIXED_TEMPS[b % 4] == 0.0)
+        algo_bytes -= n_greedy * w0.K * row
     kernel = "k_sample_fused" if w0.kind == "sample" else "k_argmax_fused"
     achieved = algo_bytes / (kern_us * 1e-6) / 1e9
     step_gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
@@ -226,7 +242,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w0.name, "B": w0.B, "K": w0.K, "V": w0.V,
+        "config": {"workload": w0.name + (" per-request T (1 in 4 greedy)"
+                                          if args.workload == "mixed" else ""),
+                   "B": w0.B, "K": w0.K, "V": w0.V,
                    "logits": w0.dtype, "temperature": w0.temperature, "top_p": w0.top_p,
                    "input_sets": len(sets), "parallelism": "none (1 GPU)"},
         "requests_per_s": w0.B / (ms_per_step / 1000.0),
