@@ -54,6 +54,8 @@ def lib():
         L.oracle_tree_is_valid.restype = I
         L.oracle_kv_commit.argtypes = [P, P, P, I, I, I, I, I, I, P, P, P, I, P]
         L.oracle_kv_commit.restype = I
+        L.oracle_tree_merge.argtypes = [P, P, P, I, P, P, P, I, I, P, P, P, P, P]
+        L.oracle_tree_merge.restype = I
         _lib = L
     return _lib
 
@@ -187,6 +189,29 @@ def verify_mixed(target, draft, tokens, u_accept, u_sample, temperature, top_p=N
                 out[key][b] = r[key][0]
         out["accepted"][b] = r["accepted"][0]
         out["tokens"][b] = r["tokens"][0]
+    return out
+
+
+def tree_merge(parents1, tokens1, conf1, parents2, tokens2, conf2):
+    """Merge two trees per request under one root and route by mean
+    confidence (oracle.c, oracle_tree_merge).  Inputs [B, n_t + 1]."""
+    p1 = np.ascontiguousarray(parents1, np.int32)
+    p2 = np.ascontiguousarray(parents2, np.int32)
+    B, n1p = p1.shape
+    n2p = p2.shape[1]
+    t1 = np.ascontiguousarray(tokens1, np.int32)
+    t2 = np.ascontiguousarray(tokens2, np.int32)
+    c1 = np.ascontiguousarray(conf1, np.float32)
+    c2 = np.ascontiguousarray(conf2, np.float32)
+    N = n1p + n2p - 1
+    out = dict(parents=np.empty((B, N), np.int32), tokens=np.empty((B, N), np.int32),
+               mask=np.empty((B, N, N), np.uint8), conf=np.empty((B, 2), np.float64),
+               route=np.empty(B, np.int32))
+    rc = lib().oracle_tree_merge(_p(p1), _p(t1), _p(c1), n1p - 1, _p(p2), _p(t2), _p(c2),
+                                 n2p - 1, B, _p(out["parents"]), _p(out["tokens"]),
+                                 _p(out["mask"]), _p(out["conf"]), _p(out["route"]))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_merge: {rc}")
     return out
 
 

@@ -566,3 +566,73 @@ int oracle_kv_commit(const void *kv_in, void *kv_out, void *mirror_out, int es, 
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Merging two drafters' trees under one root (TAPS, "방법론": one target
+ * pass over both trees under an ancestor-preserving mask; "코드 예제": the
+ * block layout) and routing by confidence (TAPS: the tree whose nodes have
+ * the higher mean predicted probability).
+ *
+ * Per request: tree t (t = 1, 2) has n_t + 1 nodes in BFS order, parents
+ * [n_t + 1] (node 0 the root, parent -1; 0 <= parent[i] < i otherwise),
+ * tokens [n_t + 1], conf [n_t + 1] (the drafter's probability of each
+ * node's token; the root's entry is not used).  The merged tree has
+ * N = n1 + n2 + 1 nodes: node 0 = the shared root (tree 1's root token);
+ * nodes 1..n1 = tree 1's nodes 1..n1 with their parents; nodes
+ * n1+1..n1+n2 = tree 2's nodes 1..n2, parent 0 staying 0 and parent p > 0
+ * becoming p + n1.  The mask row of node i is its ancestor-or-self set.
+ * Confidence of a tree: the mean of conf over its non-root nodes, summed
+ * in node order in fp64 (0 for a tree without nodes); route = 1 if tree 2's
+ * is larger, else 0.  A request with an invalid tree gets route -1,
+ * parents and tokens -1, a zero mask, confidences 0.
+ * ------------------------------------------------------------------------ */
+static int parents_ok(const int32_t *p, int n) {
+  if (p[0] != -1) return 0;
+  for (int i = 1; i <= n; ++i)
+    if (p[i] < 0 || p[i] >= i) return 0;
+  return 1;
+}
+
+int oracle_tree_merge(const int32_t *parents1, const int32_t *tokens1, const float *conf1,
+                      int n1, const int32_t *parents2, const int32_t *tokens2,
+                      const float *conf2, int n2, int B, int32_t *out_parents,
+                      int32_t *out_tokens, uint8_t *out_mask, double *out_conf,
+                      int32_t *out_route) {
+  if (!parents1 || !tokens1 || !conf1 || !parents2 || !tokens2 || !conf2 || !out_parents ||
+      !out_tokens || !out_mask || !out_conf || !out_route)
+    return -1;
+  if (n1 < 0 || n2 < 0 || B < 1 || n1 + n2 + 1 > 64) return -2;
+  const int N = n1 + n2 + 1;
+  for (int b = 0; b < B; ++b) {
+    const int32_t *p1 = parents1 + (size_t)b * (n1 + 1), *p2 = parents2 + (size_t)b * (n2 + 1);
+    const int32_t *t1 = tokens1 + (size_t)b * (n1 + 1), *t2 = tokens2 + (size_t)b * (n2 + 1);
+    const float *c1 = conf1 + (size_t)b * (n1 + 1), *c2 = conf2 + (size_t)b * (n2 + 1);
+    int32_t *par = out_parents + (size_t)b * N, *tok = out_tokens + (size_t)b * N;
+    uint8_t *mask = out_mask + (size_t)b * N * N;
+    memset(mask, 0, (size_t)N * N);
+    if (!parents_ok(p1, n1) || !parents_ok(p2, n2)) {
+      for (int i = 0; i < N; ++i) par[i] = tok[i] = -1;
+      out_conf[2 * b] = out_conf[2 * b + 1] = 0.0;
+      out_route[b] = -1;
+      continue;
+    }
+    for (int i = 0; i <= n1; ++i) {
+      par[i] = p1[i];
+      tok[i] = t1[i];
+    }
+    for (int i = 1; i <= n2; ++i) {
+      par[n1 + i] = p2[i] == 0 ? 0 : p2[i] + n1;
+      tok[n1 + i] = t2[i];
+    }
+    for (int i = 0; i < N; ++i)
+      for (int j = i; j >= 0; j = par[j]) mask[(size_t)i * N + j] = 1;
+    double s1 = 0.0, s2 = 0.0;
+    for (int i = 1; i <= n1; ++i) s1 += (double)c1[i];
+    for (int i = 1; i <= n2; ++i) s2 += (double)c2[i];
+    const double m1 = n1 > 0 ? s1 / n1 : 0.0, m2 = n2 > 0 ? s2 / n2 : 0.0;
+    out_conf[2 * b] = m1;
+    out_conf[2 * b + 1] = m2;
+    out_route[b] = m2 > m1 ? 1 : 0;
+  }
+  return 0;
+}
