@@ -31,13 +31,13 @@ def test_route_by_mean_confidence():
     p2 = np.array([[-1, 0, 1]], np.int32)
     t1 = np.array([[5, 6, 7, 8]], np.int32)
     t2 = np.array([[9, 10, 11]], np.int32)
-    o = oracle.tree_merge(p1, t1, [[0.0, 0.5, 0.25, 0.75]], p2, t2, [[0.0, 0.9, 0.6]])
+    o = oracle.tree_merge(p1, t1, [[0.0, 0.5, 0.25, 0.75]], p2, t2, [[0.0, 0.875, 0.625]])
     assert o["conf"][0].tolist() == [0.5, 0.75] and o["route"][0] == 1
     o = oracle.tree_merge(p1, t1, [[0.9, 0.5, 0.5, 0.5]], p2, t2, [[0.0, 0.5, 0.5]])
     assert o["route"][0] == 0  # equal means: the first tree
     e = np.array([[-1]], np.int32)
-    o = oracle.tree_merge(e, [[3]], [[0.0]], p2, t2, [[0.0, 0.2, 0.2]])
-    assert o["conf"][0].tolist() == [0.0, 0.2] and o["route"][0] == 1
+    o = oracle.tree_merge(e, [[3]], [[0.0]], p2, t2, [[0.0, 0.25, 0.25]])
+    assert o["conf"][0].tolist() == [0.0, 0.25] and o["route"][0] == 1
     assert o["parents"][0].tolist() == [-1, 0, 1]
 
 
