@@ -52,16 +52,27 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def source_digest() -> str:
-    """sha256 over the HIP sources' code: hardware counters are only quoted
-    for the kernel code they were taken on."""
+# The sources each kernel's code comes from: its own file and the device
+# headers it includes (declaration-only headers and the host-side ABI file
+# hold no device code).
+KERNEL_SOURCES = {
+    "k_sample_fused": ("sv_sample.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
+    "k_topp_select": ("sv_topp.hip", "sv_device.hpp", "sv_layout.hpp"),
+    "k_argmax_fused": ("sv_stream.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
+    "k_kv_commit": ("sv_kv.hip", "sv_device.hpp", "sv_layout.hpp"),
+    "k_tree_merge": ("sv_merge.hip", "sv_device.hpp", "sv_layout.hpp"),
+}
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 over the code of the sources `kernel` is built from: hardware
+    counters are only quoted for the kernel code they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_verification_sample_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), encoding="utf-8") as f:
-                h.update(name.encode())
-                h.update(_code_only(f.read()).encode())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
@@ -75,7 +86,7 @@ def counters_for(workload: str, kernel: str):
     except (OSError, ValueError):
         return None
     entry = data.get(workload, {}).get(kernel)
-    if not entry or entry.get("source_sha256") != source_digest():
+    if not entry or entry.get("source_sha256") != source_digest(kernel):
         return None
     return entry.get("traffic_bytes")
 
@@ -87,9 +98,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--min-warmup-s", type=float, default=0.3,
                     help="keep warming up until this many seconds have passed")
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["kv"],
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["kv", "merge"],
                     help="c1..c5: the five settings; mixed: the headline inputs with "
-                         "per-request temperatures; kv: the KV-cache commit")
+                         "per-request temperatures; kv: the KV-cache commit; "
+                         "merge: two drafters' trees merged with confidence routing")
     ap.add_argument("--sets", type=int, default=3,
                     help="input sets rotated across steps (1 when one set is >= 512 MiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -98,11 +110,11 @@ def main():
                     help="only run a plain device copy of this many MiB, 20 times (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
-    if args.workload == "kv":
+    if args.workload in ("kv", "merge"):
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)
             sys.exit(2)
-        kv_bench(args)
+        (kv_bench if args.workload == "kv" else merge_bench)(args)
         return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
@@ -326,6 +338,78 @@ def kv_bench(args):
         "roofline": {"bound": "hbm", "kernel": "k_kv_commit", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counters_for("kv", "k_kv_commit"), "kernel_us": ms * 1000.0,
+                     "kernel_us_from": "timed region / steps", "algorithmic_bytes": algo},
+        "cpu_baseline": cpu}), flush=True)
+
+
+def merge_bench(args):
+    """Two drafters' trees merged under one root with confidence routing
+    (spec_tree_merge): B=64 requests, two random trees of 31 non-root nodes
+    each (the merged 63-node tree of the greedy tree workload).  A step is
+    one merge."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sample_amd as sv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(0)
+    B, n = 64, 31
+    host = []
+    for _ in range(2):
+        host += [np.stack([W.grow_tree(rng, n) for _ in range(B)]).astype(np.int32),
+                 rng.integers(0, 128256, (B, n + 1)).astype(np.int32),
+                 rng.random((B, n + 1)).astype(np.float32)]
+    d = [torch.from_numpy(a).to(dev) for a in host]
+    N = 2 * n + 1
+    out = dict(parents=torch.empty((B, N), dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
+               mask=torch.empty((B, N, N), dtype=torch.uint8, device=dev),
+               conf=torch.empty((B, 2), dtype=torch.float32, device=dev),
+               route=torch.empty(B, dtype=torch.int32, device=dev))
+    call = lambda: sv.tree_merge(*d, out=out)
+    call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while i < args.warmup or time.perf_counter() - t0 < args.min_warmup_s:
+        call()
+        i += 1
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    # algorithmic bytes: both trees' parents, tokens, confidences read once;
+    # merged parents, tokens, mask, means and route written once
+    algo = B * (2 * (n + 1) * 12 + N * 8 + N * N + 12)
+    achieved = algo / (ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.lib()
+        k, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_seconds:
+            oracle.tree_merge(*host)
+            k += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": k * B / el, "unit": "requests/s", "cores": 1, "kind": "oracle",
+               "sample": f"{k} full merges of B={B}, {el:.1f}s"}
+    print(json.dumps({
+        "metric": "tree merge with confidence routing: requests/s", "value": B / (ms * 1e-3),
+        "unit": "requests/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_steps_run": i, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": f"tree merge B{B} two trees of {n} nodes -> N{N}",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "k_tree_merge", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": counters_for("merge", "k_tree_merge"), "kernel_us": ms * 1000.0,
                      "kernel_us_from": "timed region / steps", "algorithmic_bytes": algo},
         "cpu_baseline": cpu}), flush=True)
 

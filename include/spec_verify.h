@@ -157,6 +157,28 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parent
                      int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* Two drafters' trees merged under one root for one target pass, with the
+ * routing score of each tree (TAPS, "방법론": merged-tree verification
+ * under an ancestor-preserving mask, the tree with the higher mean
+ * confidence preferred when one is sent; "코드 예제": the merged layout).
+ *   parents_t [B, n_t + 1] int32 (BFS order: node 0 the root with parent -1,
+ *   0 <= parent[i] < i), tokens_t [B, n_t + 1] int32, conf_t [B, n_t + 1]
+ *   float32 (the drafter's probability of each node's token; the root's is
+ *   not used), t = 1, 2; n1 + n2 + 1 = N <= 64.
+ *   out_parents / out_tokens [B, N], out_mask [B, N, N] uint8: node 0 = the
+ *   shared root (tree 1's token), nodes 1..n1 = tree 1's, n1+1..N-1 = tree
+ *   2's non-root nodes (parent 0 stays 0, parent p > 0 becomes p + n1); mask
+ *   row i = the ancestors of node i and itself.  These are the inputs of
+ *   spec_verify_tree.
+ *   out_conf [B, 2] float32 or NULL: mean conf over each tree's non-root
+ *   nodes (0 for an empty tree); out_route [B] int32 or NULL: 1 if tree 2's
+ *   mean is larger, else 0.  A request with an invalid tree gets route -1,
+ *   parents and tokens -1 and a zero mask. */
+int spec_tree_merge(const int32_t *parents1, const int32_t *tokens1, const float *conf1, int n1,
+                    const int32_t *parents2, const int32_t *tokens2, const float *conf2, int n2,
+                    int B, int32_t *out_parents, int32_t *out_tokens, uint8_t *out_mask,
+                    float *out_conf, int32_t *out_route, hipStream_t stream);
+
 /* KV-cache commit after one cycle (next to the verify: the entries of
  * rejected drafts are cut away; lotook.com explainer, section on the KV
  * cache; a drafter sharing the target's layers receives the target's entries,

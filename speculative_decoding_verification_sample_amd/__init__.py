@@ -8,7 +8,8 @@ current HIP stream.  If the library has not been built the calls raise: there
 is no fallback implementation.
 
 Entry points (same names as the C ABI, minus the ``spec_`` prefix):
-``verify_greedy``, ``verify_sample``, ``verify_mixed``, ``verify_tree``, ``kv_commit``,
+``verify_greedy``, ``verify_sample``, ``verify_mixed``, ``verify_tree``, ``tree_merge``,
+``kv_commit``,
 ``verify_workspace_bytes``, ``status_string``, ``profile_begin``,
 ``profile_end``.
 """
@@ -28,7 +29,7 @@ ERRORS = {-1: "SPEC_ERR_NULL", -2: "SPEC_ERR_SHAPE", -3: "SPEC_ERR_PARAM",
           -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_ALIGN", -6: "SPEC_ERR_HIP"}
 
 EXPORTS = ("spec_verify_workspace_bytes", "spec_verify_greedy", "spec_verify_sample",
-           "spec_verify_mixed", "spec_verify_tree", "spec_kv_commit", "spec_status_string", "spec_profile_begin",
+           "spec_verify_mixed", "spec_verify_tree", "spec_tree_merge", "spec_kv_commit", "spec_status_string", "spec_profile_begin",
            "spec_profile_end")
 
 _lib = None
@@ -61,6 +62,8 @@ def load() -> ctypes.CDLL:
     L.spec_verify_mixed.restype = I
     L.spec_verify_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, Z, P]
     L.spec_verify_tree.restype = I
+    L.spec_tree_merge.argtypes = [P, P, P, I, P, P, P, I, I, P, P, P, P, P, P]
+    L.spec_tree_merge.restype = I
     L.spec_kv_commit.argtypes = [P, P, I, I, I, I, I, I, P, P, P, I, P, P]
     L.spec_kv_commit.restype = I
     L.spec_status_string.argtypes = [I]
@@ -273,6 +276,39 @@ def verify_tree(target, parents, node_tokens, anc_mask, *, workspace=None,
                                  _ws_ptr(ws), _ws_avail(ws), _stream(dev, stream))
     if rc != SPEC_OK:
         raise SpecVerifyError(rc, "spec_verify_tree")
+    return out
+
+
+def tree_merge(parents1, tokens1, conf1, parents2, tokens2, conf2, *, stream=None,
+               out=None) -> Dict[str, object]:
+    """Merge two trees per request ([B, n_t + 1] int32 parents / tokens,
+    float32 conf) under one root.  Returns dict(parents [B, N], tokens
+    [B, N], mask [B, N, N] uint8, conf [B, 2], route [B])."""
+    torch = _torch()
+    B, n1p = parents1.shape
+    n2p = parents2.shape[1]
+    dev = parents1.device
+    for t, name, shape, dt in ((parents1, "parents1", (B, n1p), torch.int32),
+                               (tokens1, "tokens1", (B, n1p), torch.int32),
+                               (conf1, "conf1", (B, n1p), torch.float32),
+                               (parents2, "parents2", (B, n2p), torch.int32),
+                               (tokens2, "tokens2", (B, n2p), torch.int32),
+                               (conf2, "conf2", (B, n2p), torch.float32)):
+        _check(t, name, shape, dt, dev)
+    N = n1p + n2p - 1
+    out = out if out is not None else dict(
+        parents=torch.empty((B, N), dtype=torch.int32, device=dev),
+        tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
+        mask=torch.empty((B, N, N), dtype=torch.uint8, device=dev),
+        conf=torch.empty((B, 2), dtype=torch.float32, device=dev),
+        route=torch.empty(B, dtype=torch.int32, device=dev))
+    rc = load().spec_tree_merge(_ptr(parents1), _ptr(tokens1), _ptr(conf1), n1p - 1,
+                                _ptr(parents2), _ptr(tokens2), _ptr(conf2), n2p - 1, B,
+                                _ptr(out["parents"]), _ptr(out["tokens"]), _ptr(out["mask"]),
+                                _ptr(out.get("conf")), _ptr(out.get("route")),
+                                _stream(dev, stream))
+    if rc != SPEC_OK:
+        raise SpecVerifyError(rc, "spec_tree_merge")
     return out
 
 

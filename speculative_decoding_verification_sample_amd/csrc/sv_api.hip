@@ -263,6 +263,21 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parent
   return SPEC_OK;
 }
 
+int spec_tree_merge(const int32_t *parents1, const int32_t *tokens1, const float *conf1, int n1,
+                    const int32_t *parents2, const int32_t *tokens2, const float *conf2, int n2,
+                    int B, int32_t *out_parents, int32_t *out_tokens, uint8_t *out_mask,
+                    float *out_conf, int32_t *out_route, hipStream_t stream) {
+  if (!parents1 || !tokens1 || !conf1 || !parents2 || !tokens2 || !conf2 || !out_parents ||
+      !out_tokens || !out_mask)
+    return SPEC_ERR_NULL;
+  if (B < 1 || n1 < 0 || n2 < 0 || n1 + n2 + 1 > kMaxN) return SPEC_ERR_SHAPE;
+  if (sv::launch_tree_merge(parents1, tokens1, conf1, n1, parents2, tokens2, conf2, n2, B,
+                            out_parents, out_tokens, out_mask, out_conf, out_route,
+                            stream) != hipSuccess)
+    return SPEC_ERR_HIP;
+  return SPEC_OK;
+}
+
 int spec_kv_commit(void *kv, void *mirror, int elem_bytes, int L, int B, int H, int S, int D,
                    const int32_t *cache_len, const int32_t *path_len, const int32_t *path_nodes,
                    int N, int32_t *new_len, hipStream_t stream) {

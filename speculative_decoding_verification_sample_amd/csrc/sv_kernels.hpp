@@ -27,6 +27,13 @@ int resident_workgroups(int dtype);
 // top-p nucleus threshold per row (sv_topp.hip)
 hipError_t launch_topp_select(const SampleArgs &args, int dtype, hipStream_t stream);
 
+// two trees merged under one root, with confidence routing (sv_merge.hip)
+hipError_t launch_tree_merge(const int32_t *parents1, const int32_t *tokens1, const float *conf1,
+                             int n1, const int32_t *parents2, const int32_t *tokens2,
+                             const float *conf2, int n2, int B, int32_t *out_parents,
+                             int32_t *out_tokens, uint8_t *out_mask, float *out_conf,
+                             int32_t *out_route, hipStream_t stream);
+
 // KV-cache commit after a cycle (sv_kv.hip)
 hipError_t launch_kv_commit(void *kv, void *mirror, int L, int B, int H, int S, size_t row_bytes,
                             const int32_t *cache_len, const int32_t *path_len,

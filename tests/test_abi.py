@@ -154,3 +154,14 @@ def test_mixed_errors():
     assert call(temps=None) == -1
     assert call(t=None) == -1
     assert call(wsb=0) == -4
+
+
+def test_tree_merge_errors():
+    L = sv.load()
+    call = lambda **kw: L.spec_tree_merge(
+        kw.get("p1", FAKE), FAKE, FAKE, kw.get("n1", 31), kw.get("p2", FAKE), FAKE, FAKE,
+        kw.get("n2", 31), kw.get("B", 4), kw.get("op", FAKE), FAKE, kw.get("om", FAKE), None,
+        None, None)
+    for name in ("p1", "p2", "op", "om"):
+        assert call(**{name: None}) == -1, name
+    assert call(n1=33) == -2 and call(n1=-1) == -2 and call(B=0) == -2
