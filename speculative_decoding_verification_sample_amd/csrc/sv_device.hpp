@@ -132,28 +132,68 @@ __device__ __forceinline__ float tempered(float l, float m, Scale k) {
 }
 
 // ---------------------------------------------------------------------------
-// wave64 reductions
+// wave64 reductions with DPP lane moves toward lane 63: pairs and quads
+// (quad_perm), half rows and rows (mirrors), then the row broadcasts that
+// carry row 0 into row 1, row 2 into row 3 and row 1 into rows 2 and 3; the
+// total, read back from lane 63, lands in every lane.  Lanes that a move
+// leaves out keep the identity.  Every lane must be active.
 // ---------------------------------------------------------------------------
 
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t old, uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)old, (uint32_t)v);
+  const uint32_t hi = dpp_u32<CTRL, ROWS>((uint32_t)(old >> 32), (uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t lane63_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;   // with rows 1 and 3 enabled
+constexpr int kDppBcast31 = 0x143;   // with rows 2 and 3 enabled
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  const uint32_t id = __float_as_uint(-INFINITY);
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor1>(id, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor2>(id, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppHalfMirror>(id, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppMirror>(id, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppBcast15, 0xA>(id, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppBcast31, 0xC>(id, __float_as_uint(v))));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
 }
 
+// fp64 sum in a fixed order (the same for every call)
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  auto bits = [](double x) { return (uint64_t)__double_as_longlong(x); };
+  auto val = [](uint64_t x) { return __longlong_as_double((long long)x); };
+  v += val(dpp_u64<kDppXor1>(0, bits(v)));
+  v += val(dpp_u64<kDppXor2>(0, bits(v)));
+  v += val(dpp_u64<kDppHalfMirror>(0, bits(v)));
+  v += val(dpp_u64<kDppMirror>(0, bits(v)));
+  v += val(dpp_u64<kDppBcast15, 0xA>(0, bits(v)));
+  v += val(dpp_u64<kDppBcast31, 0xC>(0, bits(v)));
+  return val(lane63_u64(bits(v)));
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
-  }
-  return v;
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u64<kDppXor1>(0, v));
+  v = mx(v, dpp_u64<kDppXor2>(0, v));
+  v = mx(v, dpp_u64<kDppHalfMirror>(0, v));
+  v = mx(v, dpp_u64<kDppMirror>(0, v));
+  v = mx(v, dpp_u64<kDppBcast15, 0xA>(0, v));
+  v = mx(v, dpp_u64<kDppBcast31, 0xC>(0, v));
+  return lane63_u64(v);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

@@ -20,12 +20,13 @@
 //     scan left to right, stop at the first mismatch).  Split 0 writes the
 //     accepted drafts.
 //  2. sum the residual mass max(0, p'_n - q'_n) over the split (p'_K when all
-//     K drafts survived: the bonus token), fp32 terms into fp64, and publish.
-//  3. the request's last residual tile (dispatched after its siblings)
-//     gathers the split masses, finds the split where the cumulative mass
-//     passes u * S (inverse CDF over ascending ids), reads that split again,
-//     scans its per-group masses and one lane walks to the token.  The other
-//     residual tiles exit after publishing.
+//     K drafts survived: the bonus token), fp32 terms into fp64, keeping the
+//     and publish the split's total.
+//  3. every residual tile of the request waits for all the split totals and
+//     finds the split where the cumulative mass passes u * S (inverse CDF
+//     over ascending ids); that split's tile scans its per-lane masses and
+//     one wave walks to the token, re-reading what the tile itself just read
+//     (its own L2).  The other tiles exit.
 // With top-p the same kernel runs twice (streaming tiles only, then residual
 // tiles only) around the nucleus kernel, which fills RowStat.
 #include <algorithm>
@@ -52,6 +53,7 @@ struct DecideLds {
 struct DrawLds {
   double tot[kMaxSplitsB];  // split masses of the request
   double wsum[kThreads / 64], wprev[kThreads / 64], lanes_end;
+  double eh, et;  // the split's scalar head and tail masses
   int wfirst[kThreads / 64], wlast[kThreads / 64];
 };
 union TileLds {
@@ -109,6 +111,31 @@ __device__ __forceinline__ u32x4 load_group(const char *p, bool aligned) {
   return r;
 }
 
+// Lanes per row group in the decide: S rounded up to a power of two.
+__device__ __forceinline__ int group_lanes(int S) {
+  return S <= 1 ? 1 : S <= 2 ? 2 : S <= 4 ? 4 : S <= 8 ? 8 : 16;
+}
+
+// Maximum / fp64 sum over aligned groups of G lanes (G in 1, 2, 4, 8, 16),
+// valid in every lane of the group.  Every lane must be active.
+__device__ __forceinline__ float group_max(float v, int G) {
+  const uint32_t id = __float_as_uint(-INFINITY);
+  if (G >= 2) v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor1>(id, __float_as_uint(v))));
+  if (G >= 4) v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor2>(id, __float_as_uint(v))));
+  if (G >= 8) v = fmaxf(v, __uint_as_float(dpp_u32<kDppHalfMirror>(id, __float_as_uint(v))));
+  if (G >= 16) v = fmaxf(v, __uint_as_float(dpp_u32<kDppMirror>(id, __float_as_uint(v))));
+  return v;
+}
+__device__ __forceinline__ double group_sum(double v, int G) {
+  auto bits = [](double x) { return (uint64_t)__double_as_longlong(x); };
+  auto val = [](uint64_t x) { return __longlong_as_double((long long)x); };
+  if (G >= 2) v += val(dpp_u64<kDppXor1>(0, bits(v)));
+  if (G >= 4) v += val(dpp_u64<kDppXor2>(0, bits(v)));
+  if (G >= 8) v += val(dpp_u64<kDppHalfMirror>(0, bits(v)));
+  if (G >= 16) v += val(dpp_u64<kDppMirror>(0, bits(v)));
+  return v;
+}
+
 // Poll one (row, split) cell until it carries this call's epoch.
 __device__ __forceinline__ bool read_cell(const u64 *part_m, const u64 *part_z, size_t g,
                                           u64 epoch, float *m, double *z) {
@@ -162,6 +189,24 @@ __device__ __forceinline__ bool decide(const int32_t *tokens, const float *u_acc
       L.row_m[t] = rs.m;
       L.row_tau[t] = rs.tau;
       L.row_zk[t] = rs.zk;
+    }
+  } else if (S <= 16 && R * group_lanes(S) <= kThreads) {
+    // one lane per cell, a row's cells in a group of G lanes (S rounded up
+    // to a power of two): the row's maximum and mass by lane moves inside
+    // the group, no pass over LDS
+    const int G = group_lanes(S);
+    const int r = t / G, c = t - r * G;
+    float m = -INFINITY;
+    double z = 0.0;
+    if (r < R && c < S &&
+        !read_cell(part_m, part_z, (size_t)global_row(r) * S + c, epoch, &m, &z))
+      *flag = 0;
+    const float M = group_max(m, G);
+    const double Z = group_sum(m > -INFINITY ? z * exp2(((double)m - (double)M) * k64) : 0.0, G);
+    if (r < R && c == 0) {
+      L.row_m[r] = M;
+      L.row_tau[r] = -INFINITY;
+      L.row_zk[r] = Z;
     }
   } else if (R * S <= kMaxCells) {
     bool ok = true;
@@ -302,42 +347,54 @@ __device__ __forceinline__ void entry_range(const SplitGeo &g, int ent, int &j0,
   }
 }
 
-// Mass of this lane's body entry.  All loads are issued before any is used;
-// lanes past the body re-read its last group (never used).
+// This lane's body groups of the drawn row pair: kVecPerThreadB consecutive
+// 16-byte groups of each row.  All loads are issued before any is used; lanes past the body re-read
+// its last group (never used).  P: the target row only.
+struct LaneGroups {
+  u32x4 wt[kVecPerThreadB], wq[kVecPerThreadB];
+};
+
+template <int DT, bool P>
+__device__ __forceinline__ void load_lane(const SplitGeo &g, LaneGroups &L) {
+  constexpr int EPV = 16 / elem_bytes(DT);
+  constexpr int VB = kVecPerThreadB;
+  if (g.nvec <= 0) return;
+  const int v0 = threadIdx.x * VB;
+  const int last = g.nvec - 1;
+  const int es = elem_bytes(DT);
+  if (g.aligned) {
+    const u32x4 *pt = reinterpret_cast<const u32x4 *>(g.bt + (size_t)g.head * es);
+    const u32x4 *pq = reinterpret_cast<const u32x4 *>(g.bq + (size_t)g.head * es);
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+      const int v = min(v0 + u, last);
+      L.wt[u] = pt[v];
+      if (!P) L.wq[u] = pq[v];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+      const size_t off = (size_t)min(v0 + u, last) * EPV * es;
+      L.wt[u] = load_group<DT>(g.bt + off, false);
+      if (!P) L.wq[u] = load_group<DT>(g.bq + off, false);
+    }
+  }
+}
+
+// Mass of this lane's body entry, in element order.
 template <int DT, bool TOPP, bool P>
-__device__ __forceinline__ double lane_mass(const SplitGeo &g, const Decision &d, Scale k) {
+__device__ __forceinline__ double lane_mass(const SplitGeo &g, const LaneGroups &L,
+                                            const Decision &d, Scale k) {
   constexpr int EPV = 16 / elem_bytes(DT);
   constexpr int VB = kVecPerThreadB;
   const int v0 = threadIdx.x * VB;
   double acc = 0.0;
-  if (g.nvec > 0) {
-    const int last = g.nvec - 1;
-    const int es = elem_bytes(DT);
-    u32x4 wt[VB], wq[VB];
-    if (g.aligned) {
-      const u32x4 *pt = reinterpret_cast<const u32x4 *>(g.bt + (size_t)g.head * es);
-      const u32x4 *pq = reinterpret_cast<const u32x4 *>(g.bq + (size_t)g.head * es);
 #pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        const int v = min(v0 + u, last);
-        wt[u] = pt[v];
-        if (!P) wq[u] = pq[v];
-      }
-    } else {
+  for (int u = 0; u < VB; ++u) {
+    if (v0 + u < g.nvec) {
 #pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        const size_t off = (size_t)min(v0 + u, last) * EPV * es;
-        wt[u] = load_group<DT>(g.bt + off, false);
-        if (!P) wq[u] = load_group<DT>(g.bq + off, false);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VB; ++u) {
-      if (v0 + u < g.nvec) {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e)
-          acc += token_mass<TOPP, P>(vec_elem(wt[u], e, DT), P ? 0.f : vec_elem(wq[u], e, DT), d, k);
-      }
+      for (int e = 0; e < EPV; ++e)
+        acc += token_mass<TOPP, P>(vec_elem(L.wt[u], e, DT), P ? 0.f : vec_elem(L.wq[u], e, DT), d, k);
     }
   }
   return acc;
@@ -365,36 +422,60 @@ __device__ __forceinline__ double block_sum(double v, double *red) {
   return s;
 }
 
-// Inclusive prefix sum over a wave (lanes in order).
+// Inclusive prefix sum over a wave (lanes in order): shifts by 1, 2, 4 and 8
+// inside each row of 16 lanes, then the row totals carried forward by the
+// row broadcasts.  Every lane must be active.
 __device__ __forceinline__ double wave_incl_scan(double v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double u = __shfl_up(v, o, 64);
-    if (l >= o) v += u;
-  }
+  auto bits = [](double x) { return (uint64_t)__double_as_longlong(x); };
+  auto val = [](uint64_t x) { return __longlong_as_double((long long)x); };
+  v += val(dpp_u64<0x111>(0, bits(v)));  // row_shr:1
+  v += val(dpp_u64<0x112>(0, bits(v)));  // row_shr:2
+  v += val(dpp_u64<0x114>(0, bits(v)));  // row_shr:4
+  v += val(dpp_u64<0x118>(0, bits(v)));  // row_shr:8
+  v += val(dpp_u64<kDppBcast15, 0xA>(0, bits(v)));
+  v += val(dpp_u64<kDppBcast31, 0xC>(0, bits(v)));
   return v;
 }
 
-// The draw inside one split: entries (head, lanes, tail) with masses e_head,
-// e_lane (this thread's lane entry) and e_tail; the token is the first one
-// whose cumulative mass from the start of the split exceeds `rem`.  Returns
-// the split-relative token in every thread; if rounding leaves no crossing,
-// the last token with positive mass.  Whole workgroup.
-template <int DT, bool TOPP, bool P>
-__device__ __forceinline__ int draw_split(const SplitGeo &g, double e_head, double e_lane, double e_tail,
-                          double rem, const Decision &d, Scale k, DrawLds &D) {
-  __shared__ int s_ent;
-  __shared__ double s_base;
-  const int t = threadIdx.x, l = lane_id(), w = t >> 6;
-  // 1. the crossing entry: cumulative masses head, lanes 0..255, tail
+// Cumulative masses of a split's entries from the start of the split: this
+// lane's entry ends at `incl` and starts at `prev`.
+struct SplitScan {
+  double prev, incl;
+};
+
+// The scan part of the draw, which does not need the target u * S yet.
+// Whole workgroup; sets D.lanes_end.
+__device__ __forceinline__ SplitScan scan_split(double e_head, double e_lane, DrawLds &D) {
+  const int l = lane_id(), w = threadIdx.x >> 6;
   const double incl_w = wave_incl_scan(e_lane);
+  const double up = __shfl_up(incl_w, 1, 64);
   if (l == 63) D.wsum[w] = incl_w;
   __syncthreads();
   double off = e_head;
   for (int i = 0; i < w; ++i) off += D.wsum[i];
-  const double incl = off + incl_w;
-  const double prev = l > 0 ? off + __shfl_up(incl_w, 1, 64) : off;  // cumulative before this entry
+  SplitScan r;
+  r.incl = off + incl_w;
+  r.prev = l > 0 ? off + up : off;
+  if (threadIdx.x == kThreads - 1) D.lanes_end = r.incl;
+  __syncthreads();
+  return r;
+}
+
+// The draw inside one split: entries (head, lanes, tail) with masses e_head,
+// e_lane (this thread's lane entry, scanned into `sc`) and e_tail; the
+// token is the first one whose cumulative mass from the start of the split
+// exceeds `rem`.  Returns the split-relative token in every thread; if
+// rounding leaves no crossing, the last token with positive mass.  Whole
+// workgroup.
+template <int DT, bool TOPP, bool P>
+__device__ __forceinline__ int draw_split(const SplitGeo &g, double e_head, double e_lane,
+                                          double e_tail, const SplitScan &sc, double rem,
+                                          const Decision &d, Scale k, DrawLds &D) {
+  __shared__ int s_ent;
+  __shared__ double s_base;
+  const int t = threadIdx.x, l = lane_id(), w = t >> 6;
+  // 1. the crossing entry: cumulative masses head, lanes 0..255, tail
+  const double prev = sc.prev, incl = sc.incl;
   const uint64_t cross = __ballot(prev <= rem && rem < incl);
   const uint64_t pos = __ballot(e_lane > 0.0);
   if (l == 0) {
@@ -402,7 +483,6 @@ __device__ __forceinline__ int draw_split(const SplitGeo &g, double e_head, doub
     D.wlast[w] = pos ? w * 64 + 63 - __builtin_clzll(pos) : -1;
   }
   if (cross && l == __builtin_ctzll(cross)) D.wprev[w] = prev;
-  if (t == kThreads - 1) D.lanes_end = incl;
   __syncthreads();
   if (t == 0) {
     int ent = -1;
@@ -439,7 +519,9 @@ __device__ __forceinline__ int draw_split(const SplitGeo &g, double e_head, doub
     entry_range<DT>(g, ent, j0, j1);
     const int j = j0 + l;
     const bool in = j < j1;
-    const double v = in ? token_mass<TOPP, P>(load_elem(g.bt, j, DT), P ? 0.f : load_elem(g.bq, j, DT), d, k) : 0.0;
+    const double v =
+        in ? token_mass<TOPP, P>(load_elem(g.bt, j, DT), P ? 0.f : load_elem(g.bq, j, DT), d, k)
+           : 0.0;
     const double c = s_base + wave_incl_scan(v);
     const uint64_t hit = __ballot(in && c > rem);
     const uint64_t has = __ballot(in && v > 0.0);
@@ -450,16 +532,79 @@ __device__ __forceinline__ int draw_split(const SplitGeo &g, double e_head, doub
   return s_tok;
 }
 
+// Inverse CDF over the split masses tot[0..SB): the split where the
+// cumulative mass first exceeds u * (sum of all), and what is left of u * sum
+// at its start.  If rounding leaves no crossing, the last split with mass
+// and rem = +inf (its last token with mass is drawn); -1 if none has mass.
+__device__ __forceinline__ int pick_split(const double *tot, int SB, float u, double *rem,
+                                          double *total) {
+  double sum = 0.0;
+  for (int i = 0; i < SB; ++i) sum += tot[i];
+  const double goal = (double)u * sum;
+  double c = 0.0;
+  int split = -1, last = -1;
+  for (int i = 0; i < SB && split < 0; ++i) {
+    if (tot[i] > 0.0) last = i;
+    if (c + tot[i] > goal) split = i;
+    else c += tot[i];
+  }
+  if (split < 0) {
+    split = last;
+    c = -INFINITY;
+  }
+  *rem = goal - c;
+  *total = sum;
+  return split;
+}
+
+// pick_split over SB <= 64 masses held one per lane of a wave (lane i holds
+// split i, lanes >= SB hold 0), by an inclusive scan; the same outcome rule.
+// The whole wave calls it; the results are valid in every lane.
+__device__ __forceinline__ int pick_split_wave(double v, int SB, float u, double *rem,
+                                               double *total) {
+  const int l = lane_id();
+  const double incl = wave_incl_scan(v);
+  auto lane_val = [&](double x, int lane) {
+    const long long b = __double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)b >> 32), lane);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  };
+  const double sum = lane_val(incl, SB - 1);
+  const double goal = (double)u * sum;
+  const uint64_t hit = __ballot(l < SB && incl > goal);
+  int split;
+  double c;
+  if (hit) {
+    split = __builtin_ctzll(hit);
+    c = split > 0 ? lane_val(incl, split - 1) : 0.0;
+  } else {  // rounding: the last split with mass, to its end
+    const uint64_t pos = __ballot(l < SB && v > 0.0);
+    split = pos ? 63 - __builtin_clzll(pos) : -1;
+    c = -INFINITY;
+  }
+  *rem = goal - c;
+  *total = sum;
+  return split;
+}
+
+// Residual tile (b, s).  Every tile of the request decides, sums its split's
+// residual masses, publishes the split's total, and waits for all its
+// siblings' totals: the one tile whose split holds u * S then draws, from
+// the per-lane masses it still holds and rows it has just read.  A tile
+// only waits for siblings dispatched before it or after it; those after it
+// are the rest of one request, so at most SB - 1 tiles ever wait for work
+// not yet dispatched, far fewer than the device holds.
 template <int DT, bool TOPP>
 __device__ __forceinline__ void residual_tile(const char *target, const char *draft, const int32_t *tokens,
                               const float *u_accept, const float *u_sample, int B, int K, int V,
                               int S, int SB, double k64, Scale k, u64 epoch,
                               const u64 *part_m, const u64 *part_z, const u64 *part_x,
-                              const RowStat *rowstat, u64 *rtot, u64 *rent,
+                              const RowStat *rowstat, u64 *rtot,
                               int32_t *out_accepted, int32_t *out_tokens, float *out_p,
                               float *out_q, float *out_mass, int b, int s, ResidLds &R) {
   const int t = threadIdx.x;
-  const float us = s == SB - 1 ? u_sample[b] : 0.f;  // the drawing tile's uniform, issued early
+  const float us = u_sample[b];  // any tile may hold the crossing; issued early
   TileLds &lds = R.lds;
   Decision &sdec = R.dec;
   int &s_ok = R.ok, &s_split = R.split, &s_use_p = R.use_p;
@@ -476,30 +621,23 @@ __device__ __forceinline__ void residual_tile(const char *target, const char *dr
   const char *rt = row_ptr(target, (size_t)b * (K + 1) + d.n, V, DT);
   const char *rd = d.mode == kModeResidual ? row_ptr(draft, (size_t)b * K + d.n, V, DT) : rt;
 
-  // 2. the residual masses of split s: its entries, then its total
-  {
-    const SplitGeo g = split_geo<DT>(rt, rd, V, s);
-    const double lm = lane_mass<DT, TOPP, false>(g, d, k);
-    double hm = 0.0, tm = 0.0;
-    if (t == 0) {
-      hm = range_mass<DT, TOPP, false>(g, 0, g.head, d, k);
-      tm = range_mass<DT, TOPP, false>(g, g.tail0, g.n, d, k);
-    }
-    u64 *ent = rent + ((size_t)b * SB + s) * kEntriesB;
-    store_agent(&ent[1 + t], pack_f64(lm, epoch));
-    if (t == 0) {
-      store_agent(&ent[0], pack_f64(hm, epoch));
-      store_agent(&ent[kThreads + 1], pack_f64(tm, epoch));
-    }
-    const double tot = block_sum(lm + hm + tm, red);
-    if (t == 0) store_agent(&rtot[(size_t)b * SB + s], pack_f64(tot, epoch));
-  }
-  // only the request's last residual tile (dispatched after its siblings)
-  // gathers the split masses and draws
-  if (s != SB - 1) return;
-
-  // 3. which split holds u * S?
+  // 2. the residual masses of split s: the lane entries, head and tail, total
   DrawLds &D = lds.draw;
+  const SplitGeo g = split_geo<DT>(rt, rd, V, s);
+  LaneGroups mine;
+  load_lane<DT, false>(g, mine);
+  if (t == 0) {
+    D.eh = range_mass<DT, TOPP, false>(g, 0, g.head, d, k);
+    D.et = range_mass<DT, TOPP, false>(g, g.tail0, g.n, d, k);
+  }
+  const double lm = lane_mass<DT, TOPP, false>(g, mine, d, k);
+  const double tot = block_sum(lm + (t == 0 ? D.eh + D.et : 0.0), red);  // syncs: D.eh / D.et visible
+  if (t == 0) store_agent(&rtot[(size_t)b * SB + s], pack_f64(tot, epoch));
+  const double eh = D.eh, et = D.et;
+  // the split's own scan, while the sibling totals are on their way
+  const SplitScan sc = scan_split(eh, lm, D);
+
+  // 3. every split's total; which split holds u * S?
   {
     bool ok = true;
     for (int i = t; i < SB; i += kThreads) {
@@ -521,96 +659,81 @@ __device__ __forceinline__ void residual_tile(const char *target, const char *dr
       return;
     }
   }
+  if (SB <= 64) {  // one wave: a scan of the split masses
+    if (t < 64) {
+      double rem, total;
+      const int split = pick_split_wave(t < SB ? D.tot[t] : 0.0, SB, us, &rem, &total);
+      if (t == 0) {
+        s_use_p = !(total > 0.0);
+        s_split = split;
+        s_rem = rem;
+        s_total = total;
+      }
+    }
+  } else if (t == 0) {
+    double rem, total;
+    const int split = pick_split(D.tot, SB, us, &rem, &total);
+    s_use_p = !(total > 0.0);
+    s_split = split;
+    s_rem = rem;
+    s_total = total;
+  }
   // S <= 0 cannot happen in exact arithmetic after a rejection (the residual
   // holds at least q'(x) - p'(x) > 0); it can when p' and q' agree and the
-  // draft token has no mass under either.  Then the draw falls back to p'
-  // (recomputed here: split by split, rare and slow).
-  if (t == 0) {
-    double tot = 0.0;
-    for (int i = 0; i < SB; ++i) tot += D.tot[i];
-    s_use_p = !(tot > 0.0);
+  // draft token has no mass under either.  Then the last tile draws from p'
+  // instead (recomputed split by split: rare and slow).
+  __syncthreads();
+  if (!s_use_p) {
+    const int claim = s_split >= 0 ? s_split : SB - 1;
+    if (s != claim) return;
+    int tok = -1;
+    if (s_split >= 0) {
+      const int local = draw_split<DT, TOPP, false>(g, eh, lm, et, sc, s_rem, d, k, D);
+      if (local >= 0) tok = g.e0 + local;
+    }
+    if (t == 0) {
+      out_tokens[(size_t)b * (K + 1) + d.n] = tok;
+      if (out_mass) out_mass[b] = (float)s_total;
+    }
+    return;
+  }
+
+  // the p' fallback, by the request's last tile
+  if (s != SB - 1) return;
+  for (int i = 0; i < SB; ++i) {
+    const SplitGeo gi = split_geo<DT>(rt, rd, V, i);
+    LaneGroups li;
+    load_lane<DT, true>(gi, li);
+    double v = lane_mass<DT, TOPP, true>(gi, li, d, k);
+    if (t == 0)
+      v += range_mass<DT, TOPP, true>(gi, 0, gi.head, d, k) +
+           range_mass<DT, TOPP, true>(gi, gi.tail0, gi.n, d, k);
+    v = block_sum(v, red);
+    if (t == 0) D.tot[i] = v;
   }
   __syncthreads();
-  if (s_use_p) {
-    for (int i = 0; i < SB; ++i) {
-      const SplitGeo g = split_geo<DT>(rt, rd, V, i);
-      double v = lane_mass<DT, TOPP, true>(g, d, k);
-      if (t == 0)
-        v += range_mass<DT, TOPP, true>(g, 0, g.head, d, k) +
-             range_mass<DT, TOPP, true>(g, g.tail0, g.n, d, k);
-      v = block_sum(v, red);
-      if (t == 0) D.tot[i] = v;
+  if (t == 0) {
+    double rem, total;
+    s_split = pick_split(D.tot, SB, us, &rem, &total);
+    s_rem = rem;
+    s_total = total;
+  }
+  __syncthreads();
+  int tok = -1;
+  if (s_split >= 0) {
+    const SplitGeo gs = split_geo<DT>(rt, rd, V, s_split);
+    LaneGroups ls;
+    load_lane<DT, true>(gs, ls);
+    const double el = lane_mass<DT, TOPP, true>(gs, ls, d, k);
+    if (t == 0) {
+      D.eh = range_mass<DT, TOPP, true>(gs, 0, gs.head, d, k);
+      D.et = range_mass<DT, TOPP, true>(gs, gs.tail0, gs.n, d, k);
     }
     __syncthreads();
-  }
-  if (t == 0) {
-    double tot = 0.0;
-    for (int i = 0; i < SB; ++i) tot += D.tot[i];
-    const double goal = (double)us * tot;
-    double c = 0.0;
-    int split = -1, last = -1;
-    for (int i = 0; i < SB && split < 0; ++i) {
-      if (D.tot[i] > 0.0) last = i;
-      if (c + D.tot[i] > goal) split = i;
-      else c += D.tot[i];
-    }
-    if (split < 0) {  // rounding: no crossing; the last split with mass, to its end
-      split = last;
-      c = -INFINITY;
-    }
-    s_split = split;
-    s_rem = goal - c;
-    s_total = tot;
-  }
-  __syncthreads();
-  const int split = s_split;
-  int tok = -1;
-  if (split >= 0) {
-    // 4. the entries of the crossing split, then the walk
-    const SplitGeo g = split_geo<DT>(rt, rd, V, split);
-    double eh = 0.0, el = 0.0, et = 0.0;
-    int local;
-    if (!s_use_p) {
-      const u64 *ent = rent + ((size_t)b * SB + split) * kEntriesB;
-      bool got = false;
-      for (int it = 0; it < kSpinLimit && !got; ++it) {
-        got = unpack_f64(load_agent(&ent[1 + t]), epoch, &el);
-        if (t == 0) {
-          got = got & unpack_f64(load_agent(&ent[0]), epoch, &eh) &
-                unpack_f64(load_agent(&ent[kThreads + 1]), epoch, &et);
-        }
-        if (!got) spin_pause();
-      }
-      if (t == 0) s_ok = 1;
-      __syncthreads();
-      if (!got) s_ok = 0;
-      __syncthreads();
-      if (!s_ok) {
-        if (t == 0) out_accepted[b] = -2;
-        return;
-      }
-      if (t == 0) {  // thread 0 holds head / tail
-        D.wsum[0] = eh;
-        D.wsum[1] = et;
-      }
-      __syncthreads();
-      eh = D.wsum[0];
-      et = D.wsum[1];
-      __syncthreads();
-      local = draw_split<DT, TOPP, false>(g, eh, el, et, s_rem, d, k, D);
-    } else {
-      el = lane_mass<DT, TOPP, true>(g, d, k);
-      if (t == 0) {
-        D.wsum[0] = range_mass<DT, TOPP, true>(g, 0, g.head, d, k);
-        D.wsum[1] = range_mass<DT, TOPP, true>(g, g.tail0, g.n, d, k);
-      }
-      __syncthreads();
-      eh = D.wsum[0];
-      et = D.wsum[1];
-      __syncthreads();
-      local = draw_split<DT, TOPP, true>(g, eh, el, et, s_rem, d, k, D);
-    }
-    if (local >= 0) tok = g.e0 + local;
+    const double eh2 = D.eh, et2 = D.et;
+    const SplitScan sc2 = scan_split(eh2, el, D);
+    const int local = draw_split<DT, TOPP, true>(gs, eh2, el, et2, sc2, s_rem, d, k, D);
+    if (local >= 0) tok = gs.e0 + local;
   }
   if (t == 0) {
     out_tokens[(size_t)b * (K + 1) + d.n] = tok;
@@ -809,12 +932,12 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
   if (a.rowstat)
     residual_tile<DT, true>(a.target, a.draft, a.tokens, a.u_accept, a.u_sample, B, K, V, S, SB,
                             q.k64, q.k, a.epoch, a.part_m, a.part_z, a.part_x, a.rowstat,
-                            a.rtot, a.rent, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
+                            a.rtot, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
                             a.out_mass, b, idx, rl);
   else
     residual_tile<DT, false>(a.target, a.draft, a.tokens, a.u_accept, a.u_sample, B, K, V, S,
                              SB, q.k64, q.k, a.epoch, a.part_m, a.part_z, a.part_x, a.rowstat,
-                             a.rtot, a.rent, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
+                             a.rtot, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
                              a.out_mass, b, idx, rl);
 }
 
