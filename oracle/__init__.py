@@ -36,7 +36,7 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
             build()
         L = ctypes.CDLL(LIB)
         P = ctypes.c_void_p
@@ -56,6 +56,10 @@ def lib():
         L.oracle_kv_commit.restype = I
         L.oracle_tree_merge.argtypes = [P, P, P, I, P, P, P, I, I, P, P, P, P, P]
         L.oracle_tree_merge.restype = I
+        L.oracle_lmhead_logits.argtypes = [P, P, I, I, I, P, P]
+        L.oracle_lmhead_logits.restype = I
+        L.oracle_lmhead_greedy.argtypes = [P, P, P, I, I, I, I, P, P, P]
+        L.oracle_lmhead_greedy.restype = I
         _lib = L
     return _lib
 
@@ -127,6 +131,42 @@ def verify_greedy(target, tokens):
                                     _p(out["accepted"]), _p(out["tokens"]), _p(out["argmax"]))
     if rc != 0:
         raise ValueError(f"oracle_verify_greedy: {rc}")
+    return out
+
+
+def lmhead_logits(hidden, weight, absdot=False):
+    """Logits of hidden-state rows against the vocabulary matrix (oracle.c,
+    oracle_lmhead_logits): hidden [R, d], weight [V, d] as bf16 bit patterns
+    (uint16).  Returns fp64 logits [R, V] (and sum |h w| [R, V] if asked)."""
+    h = np.ascontiguousarray(hidden, np.uint16)
+    w = np.ascontiguousarray(weight, np.uint16)
+    R, d = h.shape
+    V, d2 = w.shape
+    assert d == d2
+    logits = np.empty((R, V), np.float64)
+    ad = np.empty((R, V), np.float64) if absdot else None
+    rc = lib().oracle_lmhead_logits(_p(h), _p(w), R, d, V, _p(logits), _p(ad))
+    if rc != 0:
+        raise ValueError(f"oracle_lmhead_logits: {rc}")
+    return (logits, ad) if absdot else logits
+
+
+def lmhead_greedy(hidden, weight, tokens):
+    """Greedy verification on logits computed from hidden states (oracle.c,
+    oracle_lmhead_greedy): hidden [B, K+1, d], weight [V, d] bf16 bits."""
+    h = np.ascontiguousarray(hidden, np.uint16)
+    w = np.ascontiguousarray(weight, np.uint16)
+    B, K1, d = h.shape
+    K = K1 - 1
+    V = w.shape[0]
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    assert tokens.shape == (B, K) and w.shape == (V, d)
+    out = dict(accepted=np.empty(B, np.int32), tokens=np.empty((B, K + 1), np.int32),
+               argmax=np.empty((B, K + 1), np.int32))
+    rc = lib().oracle_lmhead_greedy(_p(h), _p(w), _p(tokens), B, K, d, V, _p(out["accepted"]),
+                                    _p(out["tokens"]), _p(out["argmax"]))
+    if rc != 0:
+        raise ValueError(f"oracle_lmhead_greedy: {rc}")
     return out
 
 

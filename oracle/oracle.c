@@ -403,6 +403,96 @@ int oracle_verify_greedy(const void *target, int dtype, const int32_t *tokens,
 }
 
 /* ------------------------------------------------------------------ */
+/* The target's logits from its final hidden states and the vocabulary
+ * matrix, fused in front of greedy verification.  The one target pass of
+ * [LOTOOK]'s four steps ends in this product: l[r][v] = sum_k h[r][k] *
+ * w[v][k], h and w bf16 bit patterns.  Every product is exact in fp64; the
+ * sum runs in k order in fp64.  absdot[r][v] = sum_k |h[r][k] w[v][k]|
+ * bounds the rounding of any fp32 evaluation of the same sum (by
+ * (d - 1) 2^-24 absdot / (1 - (d - 1) 2^-24), whatever the order).      */
+
+static double bf16_value(uint16_t bits) {
+  const uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static void lmhead_row(const uint16_t *hrow, const uint16_t *weight, int d, int V, double *h,
+                       double *logits, double *absdot) {
+  for (int k = 0; k < d; ++k) h[k] = bf16_value(hrow[k]);
+  for (int v = 0; v < V; ++v) {
+    const uint16_t *w = weight + (size_t)v * d;
+    double s = 0.0, a = 0.0;
+    for (int k = 0; k < d; ++k) {
+      const double p = h[k] * bf16_value(w[k]);
+      s += p;
+      a += fabs(p);
+    }
+    logits[v] = s;
+    if (absdot) absdot[v] = a;
+  }
+}
+
+int oracle_lmhead_logits(const uint16_t *hidden, const uint16_t *weight, int R, int d, int V,
+                         double *out_logits, double *out_absdot) {
+  if (!hidden || !weight || !out_logits) return -1;
+  if (R < 1 || d < 1 || V < 1) return -2;
+  double *h = (double *)malloc(sizeof(double) * (size_t)d);
+  if (!h) return -3;
+  for (int r = 0; r < R; ++r)
+    lmhead_row(hidden + (size_t)r * d, weight, d, V, h, out_logits + (size_t)r * V,
+               out_absdot ? out_absdot + (size_t)r * V : NULL);
+  free(h);
+  return 0;
+}
+
+/* Greedy verification on the fused logits: the top choice of each of the
+ * K+1 rows (lowest id on ties), then the rule of oracle_verify_greedy.  */
+int oracle_lmhead_greedy(const uint16_t *hidden, const uint16_t *weight, const int32_t *tokens,
+                         int B, int K, int d, int V, int32_t *out_accepted, int32_t *out_tokens,
+                         int32_t *out_argmax) {
+  if (!hidden || !weight || !tokens || !out_accepted || !out_tokens) return -1;
+  if (B < 1 || K < 1 || d < 1 || V < 1) return -2;
+  double *h = (double *)malloc(sizeof(double) * (size_t)d);
+  double *row = (double *)malloc(sizeof(double) * (size_t)V);
+  int32_t *a = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
+  if (!h || !row || !a) {
+    free(h);
+    free(row);
+    free(a);
+    return -3;
+  }
+  for (int b = 0; b < B; ++b) {
+    for (int i = 0; i <= K; ++i) {
+      lmhead_row(hidden + ((size_t)b * (K + 1) + i) * d, weight, d, V, h, row, NULL);
+      int best = 0;
+      for (int v = 1; v < V; ++v)
+        if (row[v] > row[best]) best = v; /* strict: ties keep the lower id */
+      a[i] = best;
+    }
+    const int32_t *tok = tokens + (size_t)b * K;
+    int n = K;
+    for (int i = 0; i < K; ++i)
+      if (tok[i] != a[i]) {
+        n = i;
+        break;
+      }
+    int32_t *ot = out_tokens + (size_t)b * (K + 1);
+    for (int i = 0; i <= K; ++i) ot[i] = -1;
+    for (int i = 0; i < n; ++i) ot[i] = tok[i];
+    ot[n] = a[n];
+    out_accepted[b] = n;
+    if (out_argmax)
+      for (int i = 0; i <= K; ++i) out_argmax[(size_t)b * (K + 1) + i] = a[i];
+  }
+  free(h);
+  free(row);
+  free(a);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* greedy verification of a merged tree ([TAPS] "방법론": one target pass
  * over all paths under an ancestor-preserving mask, keep the longest
  * accepted path).                                                       */

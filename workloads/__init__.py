@@ -418,3 +418,71 @@ def kv_commit_workload(seed: int = 0, L: int = 32, B: int = 32, H: int = 8, S: i
         path_nodes = None
     mir = r_kv.integers(0, 1 << 16, size=kv.shape, dtype=np.uint16) if mirror else None
     return KVWorkload(name, kv, cache_len, path_len, path_nodes, N, mir)
+
+
+# --------------------------------------------------------------------------
+# hidden states and a vocabulary matrix for the fused LM-head front end
+# --------------------------------------------------------------------------
+
+LMHEAD_CFG = 7  # seed-sequence slot of the LM-head workload
+
+
+@dataclasses.dataclass
+class LMHeadWorkload:
+    name: str
+    hidden: np.ndarray        # [B, K+1, d] uint16 (bf16 bits)
+    weight: np.ndarray        # [V, d] uint16 (bf16 bits)
+    tokens: np.ndarray        # [B, K] int32 draft tokens
+    intended: np.ndarray      # [B, K+1] int32: the token each row was built to favour
+
+    @property
+    def B(self) -> int:
+        return self.hidden.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.hidden.shape[1] - 1
+
+    @property
+    def d(self) -> int:
+        return self.hidden.shape[2]
+
+    @property
+    def V(self) -> int:
+        return self.weight.shape[0]
+
+
+def lmhead_workload(seed: int = 0, B: int = 64, K: int = 5, d: int = 4096, V: int = 128256,
+                    integer: bool = False, signal: float = 0.75, agree: float = 0.7,
+                    name: str = "lmhead") -> LMHeadWorkload:
+    """Final hidden states and an LM-head matrix (Llama-3-8B-sized by
+    default: d = 4096, V = 128256, bf16) for B requests of K drafts.
+
+    Real-valued: W ~ N(0, 1/d); each row of H is N(0, 1) noise, plus, with
+    probability `signal`, 0.5 sqrt(d) times the weight row of a uniformly
+    drawn intended token (which then stands far above the rest); rows without
+    it have Gaussian logits with close runners-up.  Integer-valued
+    (`integer`): W in [-3, 3], noise in [-3, 3] plus twice the intended
+    token's row, so that every logit is an integer below 2^24 and any fp32
+    evaluation is exact.  Draft tokens: the intended token of the position
+    with probability `agree`, else a uniform id (the stand-in drafter)."""
+    r = rngs(LMHEAD_CFG, seed)
+    g_w, g_h, g_t = r["logits"], r["noise"], r["tokens"]
+    intended = g_t.integers(0, V, size=(B, K + 1)).astype(np.int32)
+    has = g_t.random((B, K + 1)) < signal
+    if integer:
+        w32 = g_w.integers(-3, 4, size=(V, d)).astype(np.float32)
+        h32 = g_h.integers(-3, 4, size=(B, K + 1, d)).astype(np.float32)
+        h32 += np.where(has[..., None], 2.0 * w32[intended], 0.0).astype(np.float32)
+    else:
+        w32 = (g_w.standard_normal((V, d), dtype=np.float32) * np.float32(1.0 / np.sqrt(d)))
+        h32 = g_h.standard_normal((B, K + 1, d), dtype=np.float32)
+        w_b = bf16_bits_to_f32(f32_to_bf16_bits(w32))
+        h32 += np.where(has[..., None], np.float32(0.5 * np.sqrt(d)) * w_b[intended],
+                        np.float32(0.0)).astype(np.float32)
+    weight = f32_to_bf16_bits(w32)
+    hidden = f32_to_bf16_bits(h32)
+    agree_mask = g_t.random((B, K)) < agree
+    uniform = g_t.integers(0, V, size=(B, K)).astype(np.int32)
+    tokens = np.where(agree_mask, intended[:, :K], uniform).astype(np.int32)
+    return LMHeadWorkload(name, hidden, weight, tokens, intended)
