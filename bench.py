@@ -31,6 +31,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "verified logit-positions/s and % peak HBM GB/s at B=64 K=8 V=128256 bf16"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 MALL_BYTES = 256 << 20  # MI355X memory-side (Infinity) cache
 WORKLOADS = {"c1": 0, "c2": 1, "c3": 2, "c4": 3, "c5": 4, "mixed": 2}
@@ -61,6 +62,7 @@ KERNEL_SOURCES = {
     "k_argmax_fused": ("sv_stream.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
     "k_kv_commit": ("sv_kv.hip", "sv_device.hpp", "sv_layout.hpp"),
     "k_tree_merge": ("sv_merge.hip", "sv_device.hpp", "sv_layout.hpp"),
+    "k_lmhead_argmax": ("sv_lmhead.hip", "sv_device.hpp", "sv_layout.hpp"),
 }
 
 
@@ -98,10 +100,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--min-warmup-s", type=float, default=0.3,
                     help="keep warming up until this many seconds have passed")
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["kv", "merge"],
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["kv", "merge", "lmhead"],
                     help="c1..c5: the five settings; mixed: the headline inputs with "
                          "per-request temperatures; kv: the KV-cache commit; "
-                         "merge: two drafters' trees merged with confidence routing")
+                         "merge: two drafters' trees merged with confidence routing; "
+                         "lmhead: greedy verify with the LM head fused in front")
     ap.add_argument("--sets", type=int, default=3,
                     help="input sets rotated across steps (1 when one set is >= 512 MiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -110,11 +113,11 @@ def main():
                     help="only run a plain device copy of this many MiB, 20 times (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
-    if args.workload in ("kv", "merge"):
+    if args.workload in ("kv", "merge", "lmhead"):
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)
             sys.exit(2)
-        (kv_bench if args.workload == "kv" else merge_bench)(args)
+        {"kv": kv_bench, "merge": merge_bench, "lmhead": lmhead_bench}[args.workload](args)
         return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
@@ -411,6 +414,99 @@ def merge_bench(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": counters_for("merge", "k_tree_merge"), "kernel_us": ms * 1000.0,
                      "kernel_us_from": "timed region / steps", "algorithmic_bytes": algo},
+        "cpu_baseline": cpu}), flush=True)
+
+
+def lmhead_bench(args):
+    """Greedy verification with the target's LM head fused in front
+    (spec_lmhead_greedy): B=64 requests of K=5 drafts, hidden size 4096,
+    vocabulary 128256 (a Llama-3-8B-sized head, bf16, random weights).  A
+    step is one call (the GEMM-with-argmax launch and the decide launch).
+    Also timed: the unfused path on the same inputs (torch's bf16 matmul
+    writing the logits, then spec_verify_greedy)."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sample_amd as sv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    wl = W.lmhead_workload(seed=0)
+    B, K, d, V = wl.B, wl.K, wl.d, wl.V
+    M = B * (K + 1)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    hid, wgt = up(wl.hidden), up(wl.weight)
+    tok = torch.from_numpy(wl.tokens).to(dev)
+    ws = torch.empty(sv.load().spec_lmhead_workspace_bytes(B, K, d, V) + 256, dtype=torch.uint8,
+                     device=dev)
+    out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+    call = lambda: sv.lmhead_greedy(hid, wgt, tok, workspace=ws, out=out)
+
+    def timed(fn, steps, warmup_s):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = 0
+        while n < args.warmup or time.perf_counter() - t0 < warmup_s:
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, n
+
+    ms, nwarm = timed(call, args.steps, args.min_warmup_s)
+    mean_acc = float(out["accepted"].float().mean())
+    # unfused comparison: logits materialised by torch's bf16 matmul
+    hb, wb = hid.view(torch.bfloat16).view(M, d), wgt.view(torch.bfloat16)
+    logits = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+    gout = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+
+    def unfused():
+        logits.copy_(torch.nn.functional.linear(hb, wb))
+        sv.verify_greedy(logits.view(B, K + 1, V), tok, out=gout)
+
+    ums, _ = timed(unfused, max(10, args.steps // 4), 0.1)
+    flops = 2.0 * M * d * V
+    tflops = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.lib()
+        rows, t1 = 0, time.perf_counter()
+        h2 = wl.hidden.reshape(M, d)
+        while time.perf_counter() - t1 < args.cpu_seconds:
+            oracle.lmhead_logits(h2[rows % M:rows % M + 1], wl.weight)
+            rows += 1
+        el = time.perf_counter() - t1
+        cpu = {"value": rows / el, "unit": "positions/s", "cores": 1, "kind": "oracle",
+               "sample": f"{rows} rows of logits (d {d} x V {V}, fp64) in {el:.1f}s; the argmax "
+                         "and greedy rule on top are negligible"}
+    print(json.dumps({
+        "metric": "verified logit-positions/s (fused LM head + greedy verify)",
+        "value": M / (ms * 1e-3), "unit": "positions/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "warmup_steps_run": nwarm, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random weights)",
+        "config": {"workload": f"lmhead greedy B{B} K{K} d{d} V{V} bf16",
+                   "mean_accepted": mean_acc, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "k_lmhead_argmax", "achieved": tflops,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": counters_for("lmhead", "k_lmhead_argmax"),
+                     "kernel_us": ms * 1000.0,
+                     "kernel_us_from": "timed region / steps (both launches of the call)",
+                     "algorithmic_flops": flops, "weight_bytes": V * d * 2,
+                     "hbm_gbs_weight_stream": V * d * 2 / (ms * 1e-3) / 1e9},
+        "unfused": {"us_per_step": ums * 1000.0,
+                    "what": "torch.matmul bf16 logits [M, V] + spec_verify_greedy"},
         "cpu_baseline": cpu}), flush=True)
 
 

@@ -157,6 +157,27 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parent
                      int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* The target's LM head fused in front of greedy verification: the logits
+ * l[r][v] = sum_k hidden[r][k] * weight[v][k] of the K+1 target positions
+ * are formed on the matrix cores and reduced straight to each row's top
+ * choice; they are never written to memory (lotook.com explainer, the four
+ * steps: one target pass yields the K+1 distributions; FAQ: greedy accepts a
+ * draft only if it is the top choice).
+ *   hidden [B, K+1, d] bf16 (the target's final hidden states), weight
+ *   [V, d] bf16 (the vocabulary matrix, one row per token), both row-major
+ *   and 16-byte aligned; d a multiple of 32; 1 <= K <= 63.
+ *   Products of bf16 values are exact and accumulate in fp32 (the order of
+ *   accumulation is not specified); ties in a row go to the lowest id.
+ *   out_accepted [B], out_tokens [B, K+1] as spec_verify_greedy;
+ *   out_argmax [B, K+1] int32 or NULL: each row's top choice.
+ *   workspace: spec_lmhead_workspace_bytes() bytes, 256-byte aligned, no
+ *   clearing needed.  Two launches on `stream`. */
+size_t spec_lmhead_workspace_bytes(int B, int K, int d, int V);
+int spec_lmhead_greedy(const void *hidden, const void *weight, const int32_t *draft_tokens, int B,
+                       int K, int d, int V, int32_t *out_accepted, int32_t *out_tokens,
+                       int32_t *out_argmax, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
 /* Two drafters' trees merged under one root for one target pass, with the
  * routing score of each tree (TAPS, "방법론": merged-tree verification
  * under an ancestor-preserving mask, the tree with the higher mean

@@ -29,7 +29,8 @@ ERRORS = {-1: "SPEC_ERR_NULL", -2: "SPEC_ERR_SHAPE", -3: "SPEC_ERR_PARAM",
           -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_ALIGN", -6: "SPEC_ERR_HIP"}
 
 EXPORTS = ("spec_verify_workspace_bytes", "spec_verify_greedy", "spec_verify_sample",
-           "spec_verify_mixed", "spec_verify_tree", "spec_tree_merge", "spec_kv_commit", "spec_status_string", "spec_profile_begin",
+           "spec_verify_mixed", "spec_verify_tree", "spec_tree_merge",
+           "spec_lmhead_greedy", "spec_lmhead_workspace_bytes", "spec_kv_commit", "spec_status_string", "spec_profile_begin",
            "spec_profile_end")
 
 _lib = None
@@ -62,6 +63,10 @@ def load() -> ctypes.CDLL:
     L.spec_verify_mixed.restype = I
     L.spec_verify_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, Z, P]
     L.spec_verify_tree.restype = I
+    L.spec_lmhead_workspace_bytes.argtypes = [I, I, I, I]
+    L.spec_lmhead_workspace_bytes.restype = ctypes.c_size_t
+    L.spec_lmhead_greedy.argtypes = [P, P, P, I, I, I, I, P, P, P, P, ctypes.c_size_t, P]
+    L.spec_lmhead_greedy.restype = I
     L.spec_tree_merge.argtypes = [P, P, P, I, P, P, P, I, I, P, P, P, P, P, P]
     L.spec_tree_merge.restype = I
     L.spec_kv_commit.argtypes = [P, P, I, I, I, I, I, I, P, P, P, I, P, P]
@@ -276,6 +281,45 @@ def verify_tree(target, parents, node_tokens, anc_mask, *, workspace=None,
                                  _ws_ptr(ws), _ws_avail(ws), _stream(dev, stream))
     if rc != SPEC_OK:
         raise SpecVerifyError(rc, "spec_verify_tree")
+    return out
+
+
+def lmhead_greedy(hidden, weight, tokens, *, argmax: bool = False, workspace=None,
+                  stream=None, out=None) -> Dict[str, object]:
+    """Greedy verification with the target's LM head fused in front: hidden
+    [B, K+1, d] and weight [V, d] bf16 (torch.bfloat16 or int16 bit
+    patterns), tokens [B, K] int32.  Returns dict(accepted [B], tokens
+    [B, K+1], argmax [B, K+1] if asked)."""
+    torch = _torch()
+    B, K1, d = hidden.shape
+    K = K1 - 1
+    V = weight.shape[0]
+    dev = hidden.device
+    for t, name, shape in ((hidden, "hidden", (B, K1, d)), (weight, "weight", (V, d))):
+        if tuple(t.shape) != shape or t.dtype not in (torch.bfloat16, torch.int16) or t.device != dev:
+            raise ValueError(f"{name}: expected bf16 {shape} on {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+    _check(tokens, "tokens", (B, K), torch.int32, dev)
+    L = load()
+    need = L.spec_lmhead_workspace_bytes(B, K, d, V)
+    if need == 0:
+        raise SpecVerifyError(-2, "spec_lmhead_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr()
+    ws_off = (-ws_ptr) % 256
+    out = out if out is not None else dict(
+        accepted=torch.empty(B, dtype=torch.int32, device=dev),
+        tokens=torch.empty((B, K1), dtype=torch.int32, device=dev))
+    if argmax and "argmax" not in out:
+        out["argmax"] = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    rc = L.spec_lmhead_greedy(_ptr(hidden), _ptr(weight), _ptr(tokens), B, K, d, V,
+                              _ptr(out["accepted"]), _ptr(out["tokens"]), _ptr(out.get("argmax")),
+                              ctypes.c_void_p(ws_ptr + ws_off), workspace.numel() - ws_off,
+                              _stream(dev, stream))
+    if rc != SPEC_OK:
+        raise SpecVerifyError(rc, "spec_lmhead_greedy")
     return out
 
 

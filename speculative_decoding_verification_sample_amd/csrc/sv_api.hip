@@ -263,6 +263,41 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parent
   return SPEC_OK;
 }
 
+// ---- LM head fused with greedy verification ----
+static int lmhead_shape(long B, long K, long d, long V) {
+  if (B < 1 || K < 1 || K > kMaxK || d < 32 || d % 32 != 0 || d > (1L << 20) || V < 1 ||
+      V > 0x7FFFFFFFL)
+    return SPEC_ERR_SHAPE;
+  const long M = B * (K + 1);
+  const long RT = (M + 127) / 128, VT = (V + 255) / 256;
+  if (M > (1L << 24) || (VT + 7) / 8 * 8 * RT > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
+  return SPEC_OK;
+}
+
+size_t spec_lmhead_workspace_bytes(int B, int K, int d, int V) {
+  if (lmhead_shape(B, K, d, V) != SPEC_OK) return 0;
+  return (size_t)B * (size_t)(K + 1) * (size_t)sv::lmhead_vocab_tiles(V) * sizeof(uint64_t);
+}
+
+int spec_lmhead_greedy(const void *hidden, const void *weight, const int32_t *draft_tokens, int B,
+                       int K, int d, int V, int32_t *out_accepted, int32_t *out_tokens,
+                       int32_t *out_argmax, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  if (!hidden || !weight || !draft_tokens || !out_accepted || !out_tokens || !workspace)
+    return SPEC_ERR_NULL;
+  int rc = lmhead_shape(B, K, d, V);
+  if (rc) return rc;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 256))
+    return SPEC_ERR_ALIGN;
+  if (workspace_bytes < spec_lmhead_workspace_bytes(B, K, d, V)) return SPEC_ERR_WORKSPACE;
+  prof_before(stream);
+  const hipError_t e = sv::launch_lmhead_greedy(hidden, weight, draft_tokens, B, K, d, V,
+                                                out_accepted, out_tokens, out_argmax,
+                                                (uint64_t *)workspace, stream);
+  prof_after(stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 int spec_tree_merge(const int32_t *parents1, const int32_t *tokens1, const float *conf1, int n1,
                     const int32_t *parents2, const int32_t *tokens2, const float *conf2, int n2,
                     int B, int32_t *out_parents, int32_t *out_tokens, uint8_t *out_mask,

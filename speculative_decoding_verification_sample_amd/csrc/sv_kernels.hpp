@@ -34,6 +34,13 @@ hipError_t launch_tree_merge(const int32_t *parents1, const int32_t *tokens1, co
                              int32_t *out_tokens, uint8_t *out_mask, float *out_conf,
                              int32_t *out_route, hipStream_t stream);
 
+// LM head fused with greedy verification (sv_lmhead.hip)
+int lmhead_vocab_tiles(int V);
+hipError_t launch_lmhead_greedy(const void *hidden, const void *weight, const int32_t *tokens,
+                                int B, int K, int d, int V, int32_t *out_accepted,
+                                int32_t *out_tokens, int32_t *out_argmax, uint64_t *part,
+                                hipStream_t stream);
+
 // KV-cache commit after a cycle (sv_kv.hip)
 hipError_t launch_kv_commit(void *kv, void *mirror, int L, int B, int H, int S, size_t row_bytes,
                             const int32_t *cache_len, const int32_t *path_len,

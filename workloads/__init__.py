@@ -474,13 +474,15 @@ def lmhead_workload(seed: int = 0, B: int = 64, K: int = 5, d: int = 4096, V: in
         w32 = g_w.integers(-3, 4, size=(V, d)).astype(np.float32)
         h32 = g_h.integers(-3, 4, size=(B, K + 1, d)).astype(np.float32)
         h32 += np.where(has[..., None], 2.0 * w32[intended], 0.0).astype(np.float32)
+        weight = f32_to_bf16_bits(w32)
     else:
-        w32 = (g_w.standard_normal((V, d), dtype=np.float32) * np.float32(1.0 / np.sqrt(d)))
+        w32 = g_w.standard_normal((V, d), dtype=np.float32)
+        w32 *= np.float32(1.0 / np.sqrt(d))
+        weight = f32_to_bf16_bits(w32)
+        del w32
         h32 = g_h.standard_normal((B, K + 1, d), dtype=np.float32)
-        w_b = bf16_bits_to_f32(f32_to_bf16_bits(w32))
-        h32 += np.where(has[..., None], np.float32(0.5 * np.sqrt(d)) * w_b[intended],
+        h32 += np.where(has[..., None], np.float32(0.5 * np.sqrt(d)) * bf16_bits_to_f32(weight[intended]),
                         np.float32(0.0)).astype(np.float32)
-    weight = f32_to_bf16_bits(w32)
     hidden = f32_to_bf16_bits(h32)
     agree_mask = g_t.random((B, K)) < agree
     uniform = g_t.integers(0, V, size=(B, K)).astype(np.int32)
