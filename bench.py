@@ -470,7 +470,7 @@ def lmhead_bench(args):
                 tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
 
     def unfused():
-        logits.copy_(torch.nn.functional.linear(hb, wb))
+        torch.mm(hb, wb.t(), out=logits)
         sv.verify_greedy(logits.view(B, K + 1, V), tok, out=gout)
 
     ums, _ = timed(unfused, max(10, args.steps // 4), 0.1)
@@ -506,7 +506,7 @@ def lmhead_bench(args):
                      "algorithmic_flops": flops, "weight_bytes": V * d * 2,
                      "hbm_gbs_weight_stream": V * d * 2 / (ms * 1e-3) / 1e9},
         "unfused": {"us_per_step": ums * 1000.0,
-                    "what": "torch.matmul bf16 logits [M, V] + spec_verify_greedy"},
+                    "what": "torch.mm bf16 logits [M, V] (hipBLASLt) + spec_verify_greedy"},
         "cpu_baseline": cpu}), flush=True)
 
 

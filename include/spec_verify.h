@@ -165,7 +165,7 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parent
  * draft only if it is the top choice).
  *   hidden [B, K+1, d] bf16 (the target's final hidden states), weight
  *   [V, d] bf16 (the vocabulary matrix, one row per token), both row-major
- *   and 16-byte aligned; d a multiple of 32; 1 <= K <= 63.
+ *   and 16-byte aligned; d a multiple of 64; 1 <= K <= 63.
  *   Products of bf16 values are exact and accumulate in fp32 (the order of
  *   accumulation is not specified); ties in a row go to the lowest id.
  *   out_accepted [B], out_tokens [B, K+1] as spec_verify_greedy;

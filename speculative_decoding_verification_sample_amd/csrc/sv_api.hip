@@ -265,11 +265,11 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *parent
 
 // ---- LM head fused with greedy verification ----
 static int lmhead_shape(long B, long K, long d, long V) {
-  if (B < 1 || K < 1 || K > kMaxK || d < 32 || d % 32 != 0 || d > (1L << 20) || V < 1 ||
+  if (B < 1 || K < 1 || K > kMaxK || d < 64 || d % 64 != 0 || d > (1L << 20) || V < 1 ||
       V > 0x7FFFFFFFL)
     return SPEC_ERR_SHAPE;
   const long M = B * (K + 1);
-  const long RT = (M + 127) / 128, VT = (V + 255) / 256;
+  const long RT = (M + 383) / 384, VT = (V + 127) / 128;
   if (M > (1L << 24) || (VT + 7) / 8 * 8 * RT > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
   return SPEC_OK;
 }

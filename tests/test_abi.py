@@ -165,3 +165,19 @@ def test_tree_merge_errors():
     for name in ("p1", "p2", "op", "om"):
         assert call(**{name: None}) == -1, name
     assert call(n1=33) == -2 and call(n1=-1) == -2 and call(B=0) == -2
+
+
+def test_lmhead_errors():
+    L = sv.load()
+    assert L.spec_lmhead_workspace_bytes(2, 3, 128, 1000) == 2 * 4 * 8 * 8
+    assert L.spec_lmhead_workspace_bytes(2, 3, 96, 1000) == 0
+    call = lambda **kw: L.spec_lmhead_greedy(
+        kw.get("h", FAKE), kw.get("w", FAKE), kw.get("t", FAKE), kw.get("B", 2), kw.get("K", 3),
+        kw.get("d", 128), kw.get("V", 1000), FAKE, FAKE, None, kw.get("ws", FAKE),
+        kw.get("wsb", 1 << 20), None)
+    for name in ("h", "w", "t", "ws"):
+        assert call(**{name: None}) == -1, name
+    assert call(d=96) == -2 and call(d=0) == -2 and call(K=0) == -2 and call(K=64) == -2
+    assert call(B=0) == -2 and call(V=0) == -2
+    assert call(h=FAKE + 8) == -5 and call(ws=FAKE + 64) == -5
+    assert call(wsb=10) == -4

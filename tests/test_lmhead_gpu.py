@@ -47,8 +47,8 @@ def greedy_rule(argmax, tokens):
     return acc, toks
 
 
-@pytest.mark.parametrize("B,K,d,V", [(3, 4, 64, 1000), (30, 4, 96, 777), (2, 1, 32, 256),
-                                     (1, 63, 32, 300)])
+@pytest.mark.parametrize("B,K,d,V", [(3, 4, 64, 1000), (30, 4, 192, 777), (2, 1, 64, 128),
+                                     (1, 63, 64, 300), (80, 5, 128, 513)])
 def test_lmhead_integer_exact(B, K, d, V):
     say(f"case: lmhead integer B{B} K{K} d{d} V{V}")
     wl = W.lmhead_workload(seed=B * 7 + K, B=B, K=K, d=d, V=V, integer=True, agree=0.8)
