@@ -504,6 +504,7 @@ def lmhead_bench(args):
                      "kernel_us": ms * 1000.0,
                      "kernel_us_from": "timed region / steps (both launches of the call)",
                      "algorithmic_flops": flops, "weight_bytes": V * d * 2,
+                     "algorithmic_bytes": V * d * 2 + M * d * 2,
                      "hbm_gbs_weight_stream": V * d * 2 / (ms * 1e-3) / 1e9},
         "unfused": {"us_per_step": ums * 1000.0,
                     "what": "torch.mm bf16 logits [M, V] (hipBLASLt) + spec_verify_greedy"},

@@ -13,7 +13,7 @@
 // that the 32 lanes reading one operand fragment touch 512 contiguous bytes.
 // The epilogue finds each row's best (value, lowest column) through an LDS
 // transpose and keeps one 64-bit key per (row, vocabulary tile).
-// k_lmhead_decide: one wave per request combines its rows' partials and
+// k_lmhead_decide: one workgroup per request combines its rows' partials and
 // applies the greedy rule.
 #include "sv_device.hpp"
 #include "sv_kernels.hpp"
@@ -216,25 +216,37 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(const u32x4 *__restrict__
     }
 }
 
-// One wave per request: the top choice of each of its K+1 rows from the
-// vocabulary-tile partials, then the greedy rule (accept while the draft
+// One workgroup per request: wave w combines the vocabulary-tile partials of
+// rows w, w + 4, ... (all 64 lanes load at once, 8 partials in flight per
+// lane), then the first wave applies the greedy rule (accept while the draft
 // equals the top choice; emit the top choice at the first mismatch, or the
 // bonus after the last position).
-__global__ __launch_bounds__(64) void k_lmhead_decide(const uint64_t *__restrict__ part,
-                                                      const int32_t *__restrict__ tokens, int K,
-                                                      int VT, int32_t *__restrict__ out_accepted,
-                                                      int32_t *__restrict__ out_tokens,
-                                                      int32_t *__restrict__ out_argmax) {
-  const int b = blockIdx.x, l = threadIdx.x;
-  int am = -1;
-  for (int p = 0; p <= K; ++p) {
+__global__ __launch_bounds__(256) void k_lmhead_decide(const uint64_t *__restrict__ part,
+                                                       const int32_t *__restrict__ tokens, int K,
+                                                       int VT, int32_t *__restrict__ out_accepted,
+                                                       int32_t *__restrict__ out_tokens,
+                                                       int32_t *__restrict__ out_argmax) {
+  __shared__ int s_am[64];
+  const int b = blockIdx.x, t = threadIdx.x, l = t & 63, w = t >> 6;
+  for (int p = w; p <= K; p += 4) {
     const uint64_t *pr = part + ((size_t)b * (K + 1) + p) * VT;
     uint64_t best = 0;
-    for (int j = l; j < VT; j += 64) best = pr[j] > best ? pr[j] : best;
+    for (int j0 = 0; j0 < VT; j0 += 64 * 8) {
+      uint64_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * 64 + l;
+        v[u] = j < VT ? pr[j] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) best = v[u] > best ? v[u] : best;
+    }
     best = wave_max_u64(best);
-    const int a = (int)(0xFFFFFFFFu - (uint32_t)best);
-    if (l == p) am = a;
+    if (l == 0) s_am[p] = (int)(0xFFFFFFFFu - (uint32_t)best);
   }
+  __syncthreads();
+  if (w != 0) return;
+  const int am = l <= K ? s_am[l] : -1;
   const int x = l < K ? tokens[(size_t)b * K + l] : -1;
   const uint64_t miss = __ballot(l < K && x != am);
   const int n = miss ? __builtin_ctzll(miss) : K;
@@ -259,7 +271,7 @@ hipError_t launch_lmhead_greedy(const void *hidden, const void *weight, const in
                      (const u32x4 *)hidden, (const u32x4 *)weight, M, d, V, RT, VT, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_lmhead_decide, dim3(B), dim3(64), 0, stream, part, tokens, K, VT,
+  hipLaunchKernelGGL(k_lmhead_decide, dim3(B), dim3(256), 0, stream, part, tokens, K, VT,
                      out_accepted, out_tokens, out_argmax);
   return hipGetLastError();
 }
