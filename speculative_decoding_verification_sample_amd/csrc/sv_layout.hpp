@@ -78,12 +78,6 @@ struct Decision {
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
 
-// Residual draw records, self-validating words carrying the call's epoch
-// bits: per (request, residual split) the split's mass, and per entry of the
-// split the entry's mass.  Entries: 0 = the scalar head of the split, 1 + t =
-// the body groups of lane t (kVecPerThreadB consecutive groups), kThreads + 1
-// = the scalar tail; in that order they follow ascending token ids.
-constexpr int kEntriesB = kThreads + 2;
 // Largest number of residual splits per row (the draw stages them in LDS).
 constexpr int kMaxSplitsB = 512;
 
@@ -102,7 +96,7 @@ struct SampleArgs {
   int phase, lag;
   u64 *part_m, *part_z, *part_x;
   RowStat *rowstat;
-  u64 *rtot, *rent;
+  u64 *rtot;  // per (request, residual split): the split's mass as two tagged fp32 words
   int32_t *out_accepted, *out_tokens;
   float *out_p, *out_q, *out_mass;
 };
@@ -148,7 +142,7 @@ struct Layout {
   int SB = 0;      // residual splits per row (sampling)
   int rows = 0;    // logit rows streamed
   size_t part_m = 0, part_z = 0, part_x = 0, part_key = 0, part_tag = 0, rowstat = 0;
-  size_t rtot = 0, rent = 0;
+  size_t rtot = 0;
   // sampling: part_m / part_z hold self-validating u64 words per (row, split);
   // part_x one word per (request, position, target / draft): the logit of the
   // draft token, written by the streaming tile whose split holds it
@@ -180,8 +174,7 @@ inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p
     L.part_z = take(cells * sizeof(u64));
     L.part_x = take((size_t)B * (size_t)KN * 2 * sizeof(u64));
     L.rowstat = use_top_p ? take((size_t)L.rows * sizeof(RowStat)) : 0;
-    L.rtot = take((size_t)B * (size_t)L.SB * sizeof(u64));
-    L.rent = take((size_t)B * (size_t)L.SB * kEntriesB * sizeof(u64));
+    L.rtot = take((size_t)B * (size_t)L.SB * 2 * sizeof(u64));
   } else {
     L.part_key = take(cells * sizeof(uint64_t));
     L.part_tag = take(cells * sizeof(u64));

@@ -632,7 +632,13 @@ __device__ __forceinline__ void residual_tile(const char *target, const char *dr
   }
   const double lm = lane_mass<DT, TOPP, false>(g, mine, d, k);
   const double tot = block_sum(lm + (t == 0 ? D.eh + D.et : 0.0), red);  // syncs: D.eh / D.et visible
-  if (t == 0) store_agent(&rtot[(size_t)b * SB + s], pack_f64(tot, epoch));
+  // the split's mass as hi + lo fp32 halves, each word tagged with the
+  // epoch's low 32 bits: a stale pair validates with probability 2^-64
+  if (t == 0) {
+    const float hi = (float)tot, lo = (float)(tot - (double)hi);
+    store_agent(&rtot[((size_t)b * SB + s) * 2], pack_u32(__float_as_uint(hi), epoch));
+    store_agent(&rtot[((size_t)b * SB + s) * 2 + 1], pack_u32(__float_as_uint(lo), epoch));
+  }
   const double eh = D.eh, et = D.et;
   // the split's own scan, while the sibling totals are on their way
   const SplitScan sc = scan_split(eh, lm, D);
@@ -644,7 +650,10 @@ __device__ __forceinline__ void residual_tile(const char *target, const char *dr
       bool got = false;
       double v = 0.0;
       for (int it = 0; it < kSpinLimit && !got; ++it) {
-        got = unpack_f64(load_agent(&rtot[(size_t)b * SB + i]), epoch, &v);
+        uint32_t hi, lo;
+        got = ((int)unpack_u32(load_agent(&rtot[((size_t)b * SB + i) * 2]), epoch, &hi) &
+               (int)unpack_u32(load_agent(&rtot[((size_t)b * SB + i) * 2 + 1]), epoch, &lo)) != 0;
+        v = (double)__uint_as_float(hi) + (double)__uint_as_float(lo);
         if (!got) spin_pause();
       }
       D.tot[i] = v;
@@ -804,7 +813,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     const float *__restrict__ u_sample, const float *__restrict__ temps,
     const float *__restrict__ topps, u64 *__restrict__ part_m, u64 *__restrict__ part_z,
     u64 *__restrict__ part_x, RowStat *__restrict__ rowstat, u64 *__restrict__ rtot,
-    u64 *__restrict__ rent, int32_t *__restrict__ out_accepted,
+    int32_t *__restrict__ out_accepted,
     int32_t *__restrict__ out_tokens, float *__restrict__ out_p, float *__restrict__ out_q,
     float *__restrict__ out_mass, SampleArgs a) {
   a.target = target;
@@ -819,7 +828,6 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
   a.part_x = part_x;
   a.rowstat = rowstat;
   a.rtot = rtot;
-  a.rent = rent;
   a.out_accepted = out_accepted;
   a.out_tokens = out_tokens;
   a.out_p = out_p;
@@ -953,7 +961,7 @@ hipError_t launch_sample(const SampleArgs &args, int dtype, hipStream_t stream) 
                              : (mixed ? k_sample_fused<kF32, true> : k_sample_fused<kF32, false>);
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, stream, a.target, a.draft, a.tokens,
                      a.u_accept, a.u_sample, a.temps, a.topps, a.part_m, a.part_z, a.part_x,
-                     a.rowstat, a.rtot, a.rent, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
+                     a.rowstat, a.rtot, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
                      a.out_mass, a);
   return hipGetLastError();
 }
