@@ -194,3 +194,33 @@ def test_run_twice_bit_identical_with_poisoned_workspace():
         assert torch.equal(a[key], b[key]), key
     ref = oracle.verify_workload(w)
     check_sample(w, a, ref)
+
+
+# ---------------------------------------------------------------------------
+# without per-position diagnostics (the benchmark's call): the decision is
+# taken as soon as the positions up to the first rejection are streamed
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,kw", [
+    (0, dict()),
+    (2, dict(B=8, V=50003)),
+    (2, dict()),                      # the headline, as the benchmark times it
+    (3, dict(B=4, V=30011)),          # top-p: decided after the nucleus pass
+])
+@pytest.mark.parametrize("seed", [0, 2])
+def test_sample_without_diagnostics(cfg, kw, seed):
+    _check(W.make_config(cfg, seed=seed, **kw), diagnostics=False)
+
+
+@pytest.mark.parametrize("V,K", [(5, 3), (300, 63), (17000, 15), (16384, 8)])
+def test_sample_without_diagnostics_shapes(V, K):
+    w = W.sample_gaussian(0, B=5, K=K, V=V, dtype="f32", sigma=2.0, noise=0.7,
+                          temperature=0.9, seed=V + K, name=f"nodiag V{V} K{K}")
+    _check(w, diagnostics=False)
+
+
+def test_sample_without_diagnostics_equal_rows():
+    # draft = target: every draft accepted, the bonus row decides
+    w = W.make_config(2, seed=3, B=6, V=20011)
+    w.draft = w.target[:, :w.K].copy()
+    _check(w, diagnostics=False)
