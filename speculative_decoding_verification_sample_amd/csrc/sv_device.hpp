@@ -256,31 +256,14 @@ __device__ __forceinline__ bool block_wait_tags(const u64 *tags, int n, u64 epoc
   return *flag != 0;
 }
 
-// Self-validating 64-bit words: the epoch's bits ride in the low bits of
-// each word, so one store publishes a value and one load both reads and
-// validates it (no store-completion wait, no separate tag round trip).
-//  - an fp32 value widened to fp64 has 29 zero low bits: 24 carry tag bits
-//    and clearing them restores the value exactly;
-//  - an fp64 value gives up its low 16 bits (a relative change below 2^-36;
-//    zero stays exactly zero).
-__device__ __forceinline__ u64 tag24(u64 epoch) { return epoch & 0xFFFFFFull; }
-__device__ __forceinline__ u64 tag16(u64 epoch) { return (epoch >> 24) & 0xFFFFull; }
-
-__device__ __forceinline__ u64 pack_f32(float v, u64 epoch) {
-  return ((u64)__double_as_longlong((double)v) & ~0xFFFFFFull) | tag24(epoch);
-}
-__device__ __forceinline__ bool unpack_f32(u64 w, u64 epoch, float *v) {
-  *v = (float)__longlong_as_double((long long)(w & ~0xFFFFFFull));
-  return (w & 0xFFFFFFull) == tag24(epoch);
-}
-__device__ __forceinline__ u64 pack_f64(double v, u64 epoch) {
-  return ((u64)__double_as_longlong(v) & ~0xFFFFull) | tag16(epoch);
-}
-__device__ __forceinline__ bool unpack_f64(u64 w, u64 epoch, double *v) {
-  // clear the tag bits: 0.0 must decode as exactly 0.0 (not a denormal)
-  *v = __longlong_as_double((long long)(w & ~0xFFFFull));
-  return (w & 0xFFFFull) == tag16(epoch);
-}
+// Self-validating 64-bit words: the epoch's low 32 bits ride in the low half
+// of each word and a 32-bit payload in the high half, so one store publishes
+// a value and one load both reads and validates it (no store-completion wait,
+// no separate tag round trip). Relaxed stores to two addresses may become
+// visible in either order, so a reader can meet one fresh word beside a stale
+// one: every word therefore carries the full 32-bit tag on its own (a word
+// left by an earlier call validates only if its call's epoch agrees in all 32
+// low bits). An fp64 value travels as two such words (see split_f64).
 // a 32-bit payload in the high word, the epoch's low 32 bits in the low word
 __device__ __forceinline__ u64 pack_u32(uint32_t v, u64 epoch) {
   return ((u64)v << 32) | (epoch & 0xFFFFFFFFull);
@@ -288,6 +271,13 @@ __device__ __forceinline__ u64 pack_u32(uint32_t v, u64 epoch) {
 __device__ __forceinline__ bool unpack_u32(u64 w, u64 epoch, uint32_t *v) {
   *v = (uint32_t)(w >> 32);
   return (w & 0xFFFFFFFFull) == (epoch & 0xFFFFFFFFull);
+}
+__device__ __forceinline__ float payload_f32(u64 w) { return __uint_as_float((uint32_t)(w >> 32)); }
+// an fp64 value as an unevaluated sum hi + lo of two fp32 values (about 48
+// significant bits; exact for the values here, which lie well inside fp32's range)
+__device__ __forceinline__ void split_f64(double v, float *hi, float *lo) {
+  *hi = (float)v;
+  *lo = (float)(v - (double)*hi);
 }
 // two 16-bit indices (each -1 .. 65534) and the epoch's low 32 bits
 __device__ __forceinline__ u64 pack_idx2(int a, int b, u64 epoch) {

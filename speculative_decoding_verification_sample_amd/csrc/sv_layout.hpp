@@ -143,7 +143,8 @@ struct Layout {
   int rows = 0;    // logit rows streamed
   size_t part_m = 0, part_z = 0, part_x = 0, part_key = 0, part_tag = 0, rowstat = 0;
   size_t rtot = 0;
-  // sampling: part_m / part_z hold self-validating u64 words per (row, split);
+  // sampling: part_m one self-validating u64 word per (row, split) (the split
+  // maximum), part_z two (the split mass as fp32 hi + lo);
   // part_x one word per (request, position, target / draft): the logit of the
   // draft token, written by the streaming tile whose split holds it
   size_t total = 0;
@@ -171,7 +172,7 @@ inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p
   if (op == 1) {
     L.SB = num_splits_b(V, dtype);
     L.part_m = take(cells * sizeof(u64));
-    L.part_z = take(cells * sizeof(u64));
+    L.part_z = take(cells * 2 * sizeof(u64));
     L.part_x = take((size_t)B * (size_t)KN * 2 * sizeof(u64));
     L.rowstat = use_top_p ? take((size_t)L.rows * sizeof(RowStat)) : 0;
     L.rtot = take((size_t)B * (size_t)L.SB * 2 * sizeof(u64));

@@ -11,7 +11,8 @@
 // read (and validated) with one load, and no tile performs an atomic
 // read-modify-write.
 //
-// Streaming tile: the split's (max, tempered mass) partial, two words.
+// Streaming tile: the split's (max, tempered mass) partial, three words (the
+// maximum, and the mass as fp32 hi + lo, each word tagged on its own).
 // Residual tile (b, s), once request b's rows are all streamed:
 //  1. decide: combine the (2K+1) x S partials, evaluate p'(x_i), q'(x_i) in
 //     fp64 and the test u_i * q'(x_i) < p'(x_i); a ballot gives the first
@@ -20,8 +21,8 @@
 //     scan left to right, stop at the first mismatch).  Split 0 writes the
 //     accepted drafts.
 //  2. sum the residual mass max(0, p'_n - q'_n) over the split (p'_K when all
-//     K drafts survived: the bonus token), fp32 terms into fp64, keeping the
-//     and publish the split's total.
+//     K drafts survived: the bonus token), fp32 terms into fp64, and publish
+//     the split's total.
 //  3. every residual tile of the request waits for all the split totals and
 //     finds the split where the cumulative mass passes u * S (inverse CDF
 //     over ascending ids); that split's tile scans its per-lane masses and
@@ -141,8 +142,14 @@ __device__ __forceinline__ bool read_cell(const u64 *part_m, const u64 *part_z, 
                                           u64 epoch, float *m, double *z) {
   for (int it = 0; it < kSpinLimit; ++it) {
     const u64 mw = load_agent(&part_m[g]);
-    const u64 zw = load_agent(&part_z[g]);
-    if (unpack_f32(mw, epoch, m) & unpack_f64(zw, epoch, z)) return true;
+    const u64 hw = load_agent(&part_z[2 * g]);
+    const u64 lw = load_agent(&part_z[2 * g + 1]);
+    uint32_t mb, hb, lb;
+    if (unpack_u32(mw, epoch, &mb) & unpack_u32(hw, epoch, &hb) & unpack_u32(lw, epoch, &lb)) {
+      *m = __uint_as_float(mb);
+      *z = (double)__uint_as_float(hb) + (double)__uint_as_float(lb);
+      return true;
+    }
     spin_pause();
   }
   return false;
@@ -768,7 +775,7 @@ __device__ __forceinline__ void greedy_in_sample(const SampleArgs &a, int b) {
       for (int it = 0; it < kSpinLimit && !got; ++it) {
         uint32_t hi, lo;
         got = ((int)unpack_u32(load_agent(&a.part_m[g0 + s]), a.epoch, &hi) &
-               (int)unpack_u32(load_agent(&a.part_z[g0 + s]), a.epoch, &lo)) != 0;
+               (int)unpack_u32(load_agent(&a.part_z[2 * (g0 + s)]), a.epoch, &lo)) != 0;
         if (got) {
           const u64 key = ((u64)hi << 32) | lo;
           best = key > best ? key : best;
@@ -888,7 +895,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
       const uint64_t key = argmax_tile<DT>(row_ptr(a.target, (size_t)grow, V, DT), V, s);
       if (threadIdx.x == 0) {
         store_agent(&a.part_m[(size_t)grow * S + s], pack_u32((uint32_t)(key >> 32), a.epoch));
-        store_agent(&a.part_z[(size_t)grow * S + s], pack_u32((uint32_t)key, a.epoch));
+        store_agent(&a.part_z[2 * ((size_t)grow * S + s)], pack_u32((uint32_t)key, a.epoch));
       }
       return;
     }
@@ -921,8 +928,12 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     double Z;
     softmax_tile<DT>(rp, V, s, q.k, &M, &Z);
     if (threadIdx.x == 0) {
-      store_agent(&a.part_m[(size_t)grow * S + s], pack_f32(M, a.epoch));
-      store_agent(&a.part_z[(size_t)grow * S + s], pack_f64(Z, a.epoch));
+      const size_t g = (size_t)grow * S + s;
+      float zh, zl;
+      split_f64(Z, &zh, &zl);
+      store_agent(&a.part_m[g], pack_u32(__float_as_uint(M), a.epoch));
+      store_agent(&a.part_z[2 * g], pack_u32(__float_as_uint(zh), a.epoch));
+      store_agent(&a.part_z[2 * g + 1], pack_u32(__float_as_uint(zl), a.epoch));
       if (mine) {
         const uint32_t lx_bits = !valid ? 0xFF800000u  // -inf
                                  : DT == kBF16 ? (mis ? (w & 0xFFFF0000u) : (w << 16)) : w;

@@ -101,19 +101,13 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
 
   if (t == 0) {  // the streaming kernel has completed: every partial is in place
     const u64 *pm = part_m + (size_t)row * S;
-    const u64 *pz = part_z + (size_t)row * S;
+    const u64 *pz = part_z + (size_t)row * S * 2;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) {
-      float m;
-      unpack_f32(pm[s], 0, &m);
-      M = fmaxf(M, m);
-    }
+    for (int s = 0; s < S; ++s) M = fmaxf(M, payload_f32(pm[s]));
     double Z = 0.0;
     for (int s = 0; s < S; ++s) {
-      float m;
-      double z;
-      unpack_f32(pm[s], 0, &m);
-      unpack_f64(pz[s], 0, &z);
+      const float m = payload_f32(pm[s]);
+      const double z = (double)payload_f32(pz[2 * s]) + (double)payload_f32(pz[2 * s + 1]);
       if (m > -INFINITY) Z += z * exp2(((double)m - (double)M) * k64);
     }
     sM = M;
