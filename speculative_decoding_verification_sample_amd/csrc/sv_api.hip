@@ -268,7 +268,7 @@ static int lmhead_shape(long B, long K, long d, long V) {
       V > 0x7FFFFFFFL)
     return SPEC_ERR_SHAPE;
   const long M = B * (K + 1);
-  const long RT = (M + 383) / 384, VT = (V + 127) / 128;
+  const long RT = (M + 383) / 384, VT = sv::lmhead_vocab_tiles((int)V);
   if (M > (1L << 24) || (VT + 7) / 8 * 8 * RT > 0x7FFFFFFFL) return SPEC_ERR_SHAPE;
   return SPEC_OK;
 }

@@ -4,15 +4,18 @@
 // the four steps: one target pass yields the K+1 distributions, and the
 // greedy rule of its FAQ accepts a draft only if it is the top choice).
 //
-// k_lmhead_argmax: one workgroup (4 waves) per 384-row x 128-column tile of
-// the logits (all the rows of a verify call fit one tile, so the vocabulary
-// matrix is read once), d reduced in stages of 32 through double-buffered
-// LDS with v_mfma_f32_32x32x16_bf16 (fp32 accumulation of exact bf16
-// products).  Each wave owns 192 rows x 64 columns (6 x 2 blocks of 32 x 32).
-// LDS holds a stage as [k chunk of 8][row or column] 16-byte entries, so
-// that the 32 lanes reading one operand fragment touch 512 contiguous bytes.
-// The epilogue finds each row's best (value, lowest column) through an LDS
-// transpose and keeps one 64-bit key per (row, vocabulary tile).
+// k_lmhead_argmax: one workgroup (8 waves, two per SIMD) per 384-row x
+// 256-column tile of the logits (all the rows of a verify call fit one
+// tile, so the vocabulary matrix is read once), d reduced in stages of 64
+// with v_mfma_f32_32x32x16_bf16 (fp32 accumulation of exact bf16 products).
+// Each wave owns 192 rows x 64 columns (6 x 2 blocks of 32 x 32).  Operands
+// go from global memory straight into two LDS stages of 80 KB (loads that
+// write LDS, no register staging): while one stage is multiplied the next
+// arrives.  A stage holds each row's 128 bytes of d (eight 16-byte chunks,
+// one whole cache line, fetched by 8 lanes of one load) side by side, the
+// chunk position XOR-ed with bits 1..3 of the row, so that the 16 lanes of
+// a fragment read quarter touch 16 different bank groups.  The wide tile
+// halves the re-reads of the hidden states (every tile reads all of them).
 // k_lmhead_decide: one workgroup per request combines its rows' partials and
 // applies the greedy rule.
 #include "sv_device.hpp"
@@ -26,29 +29,32 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kLmRows = 384;   // rows per tile (12 blocks of 32)
-constexpr int kLmCols = 128;   // vocabulary columns per tile (4 blocks of 32)
-constexpr int kLmK = 32;       // d per LDS stage
-constexpr int kLmChunks = kLmK / 8;
-constexpr int kLmWaveRows = kLmRows / 2;  // each wave: 192 rows x 64 columns
-constexpr int kLmRB = kLmWaveRows / 32;   // 6 row blocks per wave
-constexpr int kLmA = kLmRows * kLmChunks / 256;  // staged 16-byte loads per thread: 6
-constexpr int kLmB = kLmCols * kLmChunks / 256;  // 2
+constexpr int kLmCols = 256;   // vocabulary columns per tile (8 blocks of 32)
+constexpr int kLmThreads = 512;
+constexpr int kLmK = 64;       // d per LDS stage
+constexpr int kLmChunks = kLmK / 8;                // 16-byte chunks per row and stage
+constexpr int kLmWaveRows = kLmRows / 2;           // each wave: 192 rows x 64 columns
+constexpr int kLmWaveCols = kLmCols / 4;
+constexpr int kLmRB = kLmWaveRows / 32;            // 6 row blocks per wave
+constexpr int kLmCB = kLmWaveCols / 32;            // 2 column blocks per wave
+constexpr int kLmEntA = kLmRows * kLmChunks;       // 3072 entries of 16 bytes
+constexpr int kLmEnt = kLmEntA + kLmCols * kLmChunks;  // 5120 entries: 80 KB a stage
+constexpr int kLmLoadsA = kLmEntA / kLmThreads;    // 6 wave loads of 1 KB per wave
+constexpr int kLmLoadsB = kLmCols * kLmChunks / kLmThreads;  // 4
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-struct StageA {
-  u32x4 v[kLmA];
-};
-struct StageB {
-  u32x4 v[kLmB];
-};
+// slot of chunk c of row (or column) r within its operand's part of a stage
+__device__ __forceinline__ int lm_entry(int r, int c) { return r * kLmChunks + (c ^ ((r >> 1) & 7)); }
+
+typedef __attribute__((address_space(3))) void *lds_ptr;
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void k_lmhead_argmax(const u32x4 *__restrict__ hidden,
-                                                       const u32x4 *__restrict__ weight,
-                                                       int M, int d, int V, int RT, int VT,
-                                                       uint64_t *__restrict__ part) {
+__global__ __launch_bounds__(kLmThreads) void k_lmhead_argmax(const u32x4 *__restrict__ hidden,
+                                                              const u32x4 *__restrict__ weight,
+                                                              int M, int d, int V, int RT, int VT,
+                                                              uint64_t *__restrict__ part) {
   // block -> (vocabulary tile vt, row tile rt): the RT row tiles of one
   // vocabulary tile share blockIdx mod 8 (one XCD) and run back to back
   const int blk = blockIdx.x;
@@ -57,146 +63,120 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(const u32x4 *__restrict__
   if (vt >= VT) return;
   const int r0 = rt * kLmRows, v0 = vt * kLmCols;
   const int t = threadIdx.x, l = t & 63, wv = t >> 6;
-  const int wr = wv >> 1, wc = wv & 1;  // wave's 192-row and 64-column part
-  const int dv = d >> 3;                // 16-byte chunks per row
+  const int wr = wv >> 2, wc = wv & 3;  // wave's 192-row and 64-column part
 
-  // one buffer: A [chunk][row], B [chunk][column], 16-byte entries (the 32
-  // lanes reading a fragment touch 512 contiguous bytes); the chunk planes
-  // are two entries longer than a row of entries, so that the 8 lanes of a
-  // store group (2 rows x 4 chunks) spread over 32 banks
-  constexpr int kPA = kLmRows + 2, kPB = kLmCols + 2;  // plane strides (entries)
-  __shared__ u32x4 sA[2][kLmChunks * kPA];
-  __shared__ u32x4 sB[2][kLmChunks * kPB];
-  __shared__ uint64_t sKey[2][kLmRows];
+  __shared__ u32x4 ring[2 * kLmEnt];
 
-  // staging: entry e = t + 256 j -> (row or column e / 4, chunk e % 4): 4
-  // lanes read a row's 64 bytes of the stage.  Rows at or past M and
-  // columns at or past V load row M-1 / column V-1 (unconditional loads keep
-  // the wait counts exact); their products only reach rows that are never
+  // Loads: wave wv fills entries (wv * n + j) * 64 .. + 64 of each operand
+  // part, lane l entry + l: row e / 8 (8 lanes read its 128 bytes) and the
+  // chunk its slot holds.  Rows at or past M and columns at or past V load
+  // row M-1 / column V-1; their products only reach rows that are never
   // written and columns the epilogue drops.
-  const u32x4 *hp[kLmA], *wp[kLmB];
+  uint32_t oa[kLmLoadsA], ob[kLmLoadsB];  // byte offsets from the tile's first row / column
 #pragma unroll
-  for (int j = 0; j < kLmA; ++j) {
-    const int e = t + 256 * j;
-    hp[j] = hidden + (size_t)min(r0 + (e >> 2), M - 1) * dv + (e & 3);
+  for (int j = 0; j < kLmLoadsA; ++j) {
+    const int e = (wv * kLmLoadsA + j) * 64 + l, r = e >> 3;
+    const int c = (e & 7) ^ ((r >> 1) & 7);
+    oa[j] = (uint32_t)((min(r0 + r, M - 1) - r0) * d + c * 8) * 2u;
   }
 #pragma unroll
-  for (int j = 0; j < kLmB; ++j) {
-    const int e = t + 256 * j;
-    wp[j] = weight + (size_t)min(v0 + (e >> 2), V - 1) * dv + (e & 3);
+  for (int j = 0; j < kLmLoadsB; ++j) {
+    const int e = (wv * kLmLoadsB + j) * 64 + l, r = e >> 3;
+    const int c = (e & 7) ^ ((r >> 1) & 7);
+    ob[j] = (uint32_t)((min(v0 + r, V - 1) - v0) * d + c * 8) * 2u;
   }
-  auto load_a = [&](int s, StageA &R) {
+  const char *hbase = reinterpret_cast<const char *>(hidden) + (size_t)r0 * d * 2;
+  const char *wbase = reinterpret_cast<const char *>(weight) + (size_t)v0 * d * 2;
+  // stage src (d from 64 src) into ring slot `slot`; 10 loads per wave
+  auto issue = [&](int slot, int src) {
+    u32x4 *base = ring + slot * kLmEnt;
+    const char *hs = hbase + src * (kLmK * 2), *ws = wbase + src * (kLmK * 2);
 #pragma unroll
-    for (int j = 0; j < kLmA; ++j) R.v[j] = hp[j][s * kLmChunks];
-  };
-  auto load_b = [&](int s, StageB &R) {
+    for (int j = 0; j < kLmLoadsA; ++j)
+      __builtin_amdgcn_global_load_lds(hs + oa[j], (lds_ptr)(base + (wv * kLmLoadsA + j) * 64), 16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < kLmB; ++j) R.v[j] = __builtin_nontemporal_load(wp[j] + s * kLmChunks);
-  };
-  auto store = [&](int buf, const StageA &A, const StageB &B) {
-#pragma unroll
-    for (int j = 0; j < kLmA; ++j) {
-      const int e = t + 256 * j;
-      sA[buf][(e & 3) * kPA + (e >> 2)] = A.v[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kLmB; ++j) {
-      const int e = t + 256 * j;
-      sB[buf][(e & 3) * kPB + (e >> 2)] = B.v[j];
-    }
+    for (int j = 0; j < kLmLoadsB; ++j)
+      __builtin_amdgcn_global_load_lds(ws + ob[j], (lds_ptr)(base + kLmEntA + (wv * kLmLoadsB + j) * 64),
+                                       16, 0, 2 /* nontemporal: the matrix is read once */);
   };
 
-  f32x16 acc[kLmRB][2];
+  f32x16 acc[kLmRB][kLmCB];
 #pragma unroll
   for (int i = 0; i < kLmRB; ++i)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < kLmCB; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][c][v] = 0.f;
 
-  // all operand fragments of the stage's two k-steps are read first, then
-  // the 24 products issue back to back
-  auto compute = [&](int buf) {
-    bf16x8 fa[2][kLmRB], fb[2][2];
+  // fragments of k-step ks (16 of d) of slot `slot`, and their 12 products
+  auto read_frags = [&](int slot, int ks, bf16x8 (&fa)[kLmRB], bf16x8 (&fb)[kLmCB]) {
+    const u32x4 *base = ring + slot * kLmEnt;
+    const int ch = ks * 2 + (l >> 5);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks * 2 + (l >> 5);
+    for (int i = 0; i < kLmRB; ++i)
+      fa[i] = as_bf16x8(base[lm_entry(wr * kLmWaveRows + i * 32 + (l & 31), ch)]);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        fb[ks][c] = as_bf16x8(sB[buf][ch * kPB + wc * 64 + c * 32 + (l & 31)]);
+    for (int c = 0; c < kLmCB; ++c)
+      fb[c] = as_bf16x8(base[kLmEntA + lm_entry(wc * kLmWaveCols + c * 32 + (l & 31), ch)]);
+  };
+  auto mma = [&](const bf16x8 (&fa)[kLmRB], const bf16x8 (&fb)[kLmCB]) {
 #pragma unroll
-      for (int i = 0; i < kLmRB; ++i)
-        fa[ks][i] = as_bf16x8(sA[buf][ch * kPA + wr * kLmWaveRows + i * 32 + (l & 31)]);
-    }
+    for (int i = 0; i < kLmRB; ++i)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < kLmRB; ++i)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][c], acc[i][c], 0, 0, 0);
-    // scheduling hint: the 16 fragment reads first, then the 24 products
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+      for (int c = 0; c < kLmCB; ++c)
+        acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[c], acc[i][c], 0, 0, 0);
   };
 
-  // The vocabulary matrix streams from HBM with four stages in flight; the
-  // hidden states (a few MB, read by every tile) come from L2 two stages
-  // ahead.  A step: the sets that held stage s (stored by the step before)
-  // take stage s + 4 / s + 2 (the last stage again near the end), stage s is
-  // multiplied, stage s + 1 is stored (past the end, a copy of the last
-  // stage lands in a buffer nothing reads).
+  // Step s: wait until this wave's loads of stage s have landed (nothing
+  // else is outstanding); the barrier makes every wave's part visible and
+  // guarantees every wave is done with stage s - 1, whose slot then takes
+  // stage s + 1 (past the end, a copy of the last stage into a slot nothing
+  // reads any more).  The accumulators take 192 of a wave's 256 registers,
+  // so a k-step's fragments are read just before its products; the other
+  // wave on the SIMD runs its products meanwhile.
   const int S = d / kLmK;
-  StageA H0, H1;
-  StageB W0, W1, W2, W3;
-  auto step = [&](int s, StageB &wcur, StageB &wnext, StageA &hcur, StageA &hnext) {
-    load_b(min(s + 4, S - 1), wcur);
-    load_a(min(s + 2, S - 1), hcur);
-    compute(s & 1);
-    store((s + 1) & 1, hnext, wnext);
-    __syncthreads();
-  };
-  load_b(0, W0);
-  load_a(0, H0);
-  load_b(min(1, S - 1), W1);
-  load_a(min(1, S - 1), H1);
-  load_b(min(2, S - 1), W2);
-  load_b(min(3, S - 1), W3);
-  store(0, H0, W0);
-  __syncthreads();
-  int s = 0;
-  for (; s + 4 <= S; s += 4) {
-    step(s, W0, W1, H0, H1);
-    step(s + 1, W1, W2, H1, H0);
-    step(s + 2, W2, W3, H0, H1);
-    step(s + 3, W3, W0, H1, H0);
+  issue(0, 0);
+  for (int s = 0; s < S; ++s) {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    issue((s + 1) & 1, min(s + 1, S - 1));
+    const int slot = s & 1;
+#pragma unroll
+    for (int ks = 0; ks < kLmK / 16; ++ks) {
+      bf16x8 fa[kLmRB], fb[kLmCB];
+      read_frags(slot, ks, fa, fb);
+      mma(fa, fb);
+    }
   }
-  if (s < S) step(s, W0, W1, H0, H1);
-  if (s + 1 < S) step(s + 1, W1, W2, H1, H0);
-  if (s + 2 < S) step(s + 2, W2, W3, H0, H1);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the ring is idle
+  __builtin_amdgcn_s_barrier();
 
   // epilogue: each row's best (value, lowest column).  Per row block the
-  // wave writes its 32 x 64 logits to LDS (the operand buffers are free
-  // now), then lane l scans columns 32 (l / 32) .. + 32 of row l % 32, and
-  // the two halves combine through one lane exchange.
-  float *sT = reinterpret_cast<float *>(&sA[0][0]) + wv * (32 * 65);
+  // wave writes its 32 x 64 logits to LDS (the ring is free now), then lane
+  // l scans columns 32 (l / 32) .. + 32 of row l % 32, and the two halves
+  // combine through one lane exchange.
+  constexpr int kT = kLmWaveCols + 1;  // transpose row stride (floats)
+  float *sT = reinterpret_cast<float *>(ring) + wv * (32 * kT);
+  uint64_t(*sKey)[kLmRows] =
+      reinterpret_cast<uint64_t(*)[kLmRows]>(reinterpret_cast<float *>(ring) + 8 * 32 * kT);
 #pragma unroll
   for (int i = 0; i < kLmRB; ++i) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < kLmCB; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-        sT[row * 65 + c * 32 + (l & 31)] = acc[i][c][v];
+        sT[row * kT + c * 32 + (l & 31)] = acc[i][c][v];
       }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     const int row = l & 31, half = l >> 5;
-    const int cbase = v0 + wc * 64 + half * 32;
+    constexpr int kHalf = kLmWaveCols / 2;
+    const int cbase = v0 + wc * kLmWaveCols + half * kHalf;
     float bv = -INFINITY;
     int bc = 0x7FFFFFFF;
-    for (int j = 0; j < 32; ++j) {
-      const float x = cbase + j < V ? sT[row * 65 + half * 32 + j] : -INFINITY;
+    for (int j = 0; j < kHalf; ++j) {
+      const float x = cbase + j < V ? sT[row * kT + half * kHalf + j] : -INFINITY;
       if (x > bv) {  // strict: equal values keep the lower column
         bv = x;
         bc = cbase + j;
@@ -209,10 +189,12 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(const u32x4 *__restrict__
     __builtin_amdgcn_wave_barrier();
   }
   __syncthreads();
-  for (int r = t; r < kLmRows; r += 256)
+  for (int r = t; r < kLmRows; r += kLmThreads)
     if (r0 + r < M) {
-      const uint64_t a = sKey[0][r], b = sKey[1][r];
-      part[(size_t)(r0 + r) * VT + vt] = a > b ? a : b;
+      uint64_t a = sKey[0][r];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) a = sKey[q][r] > a ? sKey[q][r] : a;
+      part[(size_t)(r0 + r) * VT + vt] = a;
     }
 }
 
@@ -267,7 +249,7 @@ hipError_t launch_lmhead_greedy(const void *hidden, const void *weight, const in
   const int RT = (M + kLmRows - 1) / kLmRows;
   const int VT = lmhead_vocab_tiles(V);
   const int groups = (VT + 7) / 8;
-  hipLaunchKernelGGL(k_lmhead_argmax, dim3(groups * 8 * RT), dim3(256), 0, stream,
+  hipLaunchKernelGGL(k_lmhead_argmax, dim3(groups * 8 * RT), dim3(kLmThreads), 0, stream,
                      (const u32x4 *)hidden, (const u32x4 *)weight, M, d, V, RT, VT, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -169,7 +169,8 @@ def test_tree_merge_errors():
 
 def test_lmhead_errors():
     L = sv.load()
-    assert L.spec_lmhead_workspace_bytes(2, 3, 128, 1000) == 2 * 4 * 8 * 8
+    # one 8-byte key per (row, 256-column vocabulary tile)
+    assert L.spec_lmhead_workspace_bytes(2, 3, 128, 1000) == 2 * 4 * 4 * 8
     assert L.spec_lmhead_workspace_bytes(2, 3, 96, 1000) == 0
     call = lambda **kw: L.spec_lmhead_greedy(
         kw.get("h", FAKE), kw.get("w", FAKE), kw.get("t", FAKE), kw.get("B", 2), kw.get("K", 3),
