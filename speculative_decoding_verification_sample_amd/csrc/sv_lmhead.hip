@@ -8,7 +8,8 @@
 // 256-column tile of the logits (all the rows of a verify call fit one
 // tile, so the vocabulary matrix is read once), d reduced in stages of 64
 // with v_mfma_f32_32x32x16_bf16 (fp32 accumulation of exact bf16 products).
-// Each wave owns 192 rows x 64 columns (6 x 2 blocks of 32 x 32).  Operands
+// Each wave owns 96 rows x 128 columns (3 x 4 blocks of 32 x 32: 7
+// fragment reads feed 12 products).  Operands
 // go from global memory straight into two LDS stages of 80 KB (loads that
 // write LDS, no register staging): while one stage is multiplied the next
 // arrives.  A stage holds each row's 128 bytes of d (eight 16-byte chunks,
@@ -33,10 +34,11 @@ constexpr int kLmCols = 256;   // vocabulary columns per tile (8 blocks of 32)
 constexpr int kLmThreads = 512;
 constexpr int kLmK = 64;       // d per LDS stage
 constexpr int kLmChunks = kLmK / 8;                // 16-byte chunks per row and stage
-constexpr int kLmWaveRows = kLmRows / 2;           // each wave: 192 rows x 64 columns
-constexpr int kLmWaveCols = kLmCols / 4;
-constexpr int kLmRB = kLmWaveRows / 32;            // 6 row blocks per wave
-constexpr int kLmCB = kLmWaveCols / 32;            // 2 column blocks per wave
+constexpr int kLmWaveRows = kLmRows / 4;           // each wave: 96 rows x 128 columns
+constexpr int kLmWaveCols = kLmCols / 2;
+constexpr int kLmRB = kLmWaveRows / 32;            // 3 row blocks per wave
+constexpr int kLmCB = kLmWaveCols / 32;            // 4 column blocks per wave
+constexpr int kLmColWaves = kLmCols / kLmWaveCols; // waves across the columns
 constexpr int kLmEntA = kLmRows * kLmChunks;       // 3072 entries of 16 bytes
 constexpr int kLmEnt = kLmEntA + kLmCols * kLmChunks;  // 5120 entries: 80 KB a stage
 constexpr int kLmLoadsA = kLmEntA / kLmThreads;    // 6 wave loads of 1 KB per wave
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(kLmThreads) void k_lmhead_argmax(const u32x4 *__res
   if (vt >= VT) return;
   const int r0 = rt * kLmRows, v0 = vt * kLmCols;
   const int t = threadIdx.x, l = t & 63, wv = t >> 6;
-  const int wr = wv >> 2, wc = wv & 3;  // wave's 192-row and 64-column part
+  const int wr = wv / kLmColWaves, wc = wv % kLmColWaves;  // wave's rows and columns
 
   __shared__ u32x4 ring[2 * kLmEnt];
 
@@ -85,19 +87,26 @@ __global__ __launch_bounds__(kLmThreads) void k_lmhead_argmax(const u32x4 *__res
     const int c = (e & 7) ^ ((r >> 1) & 7);
     ob[j] = (uint32_t)((min(v0 + r, V - 1) - v0) * d + c * 8) * 2u;
   }
-  const char *hbase = reinterpret_cast<const char *>(hidden) + (size_t)r0 * d * 2;
-  const char *wbase = reinterpret_cast<const char *>(weight) + (size_t)v0 * d * 2;
+  // buffer descriptors over the tile's rows / columns (32-bit lane offsets,
+  // the stage's offset in a scalar register)
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const char *>(hidden) + (size_t)r0 * d * 2), (short)0,
+      (int)((size_t)(min(M - r0, kLmRows)) * d * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const char *>(weight) + (size_t)v0 * d * 2), (short)0,
+      (int)((size_t)(min(V - v0, kLmCols)) * d * 2), 0x00020000);
   // stage src (d from 64 src) into ring slot `slot`; 10 loads per wave
   auto issue = [&](int slot, int src) {
     u32x4 *base = ring + slot * kLmEnt;
-    const char *hs = hbase + src * (kLmK * 2), *ws = wbase + src * (kLmK * 2);
+    const int so = src * (kLmK * 2);
 #pragma unroll
     for (int j = 0; j < kLmLoadsA; ++j)
-      __builtin_amdgcn_global_load_lds(hs + oa[j], (lds_ptr)(base + (wv * kLmLoadsA + j) * 64), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(base + (wv * kLmLoadsA + j) * 64), 16,
+                                               oa[j], so, 0, 0);
 #pragma unroll
     for (int j = 0; j < kLmLoadsB; ++j)
-      __builtin_amdgcn_global_load_lds(ws + ob[j], (lds_ptr)(base + kLmEntA + (wv * kLmLoadsB + j) * 64),
-                                       16, 0, 2 /* nontemporal: the matrix is read once */);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr)(base + kLmEntA + (wv * kLmLoadsB + j) * 64),
+                                               16, ob[j], so, 0, 2 /* nontemporal: read once */);
   };
 
   f32x16 acc[kLmRB][kLmCB];
@@ -152,8 +161,8 @@ __global__ __launch_bounds__(kLmThreads) void k_lmhead_argmax(const u32x4 *__res
   __builtin_amdgcn_s_barrier();
 
   // epilogue: each row's best (value, lowest column).  Per row block the
-  // wave writes its 32 x 64 logits to LDS (the ring is free now), then lane
-  // l scans columns 32 (l / 32) .. + 32 of row l % 32, and the two halves
+  // wave writes its 32 x 128 logits to LDS (the ring is free now), then lane
+  // l scans columns 64 (l / 32) .. + 64 of row l % 32, and the two halves
   // combine through one lane exchange.
   constexpr int kT = kLmWaveCols + 1;  // transpose row stride (floats)
   float *sT = reinterpret_cast<float *>(ring) + wv * (32 * kT);
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(kLmThreads) void k_lmhead_argmax(const u32x4 *__res
     if (r0 + r < M) {
       uint64_t a = sKey[0][r];
 #pragma unroll
-      for (int q = 1; q < 4; ++q) a = sKey[q][r] > a ? sKey[q][r] : a;
+      for (int q = 1; q < kLmColWaves; ++q) a = sKey[q][r] > a ? sKey[q][r] : a;
       part[(size_t)(r0 + r) * VT + vt] = a;
     }
 }
