@@ -231,6 +231,21 @@ def main():
         kern_us = 1000.0 * kern_ms / max(1, launches)
         kern_src = f"HIP events around each streaming launch, {launches} launches"
 
+    # per-call distribution: each call bracketed by its own pair of events
+    n_call = min(args.steps, 100)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_call)]
+    torch.cuda.synchronize()
+    for i in range(n_call):
+        ev[i][0].record()
+        calls[i % len(calls)]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    per_call = np.array([1000.0 * a.elapsed_time(b) for a, b in ev])
+    call_us = {"median": float(np.median(per_call)), "p10": float(np.percentile(per_call, 10)),
+               "p90": float(np.percentile(per_call, 90)), "calls": n_call,
+               "note": "each call between its own two HIP events"}
+
     ms_per_step = total_ms / args.steps
     positions = w0.positions
     value = positions / (ms_per_step / 1000.0)
@@ -239,10 +254,22 @@ def main():
         row = w0.V * (2 if w0.dtype == "bf16" else 4)
         n_greedy = sum(1 for b in range(w0.B) if MIXED_TEMPS[b % 4] == 0.0)
         algo_bytes -= n_greedy * w0.K * row
+    # the residual pass re-reads one row pair per request (the bonus draw: one
+    # row); counted here from the first call's outcomes, never in `achieved`
+    resample_bytes = 0
+    if w0.kind == "sample":
+        row = w0.V * (2 if w0.dtype == "bf16" else 4)
+        acc = first["accepted"].cpu().numpy()
+        greedy_req = ([MIXED_TEMPS[b % 4] == 0.0 for b in range(w0.B)]
+                      if args.workload == "mixed" else [False] * w0.B)
+        resample_bytes = int(sum(0 if g else (row if n == w0.K else 2 * row)
+                                 for n, g in zip(acc, greedy_req)))
     kernel = "k_sample_fused" if w0.kind == "sample" else "k_argmax_fused"
     achieved = algo_bytes / (kern_us * 1e-6) / 1e9
     step_gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
     cpu = cpu_baseline(w0, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    cpu_pool = cpu_baseline_threads(w0, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    traffic = counters_for(args.workload, kernel)
     result = {
         "metric": METRIC,
         "value": value,
@@ -267,10 +294,14 @@ def main():
         "mean_accepted": mean_accepted,
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": counters_for(args.workload, kernel),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_over_algorithmic": (traffic / algo_bytes) if traffic else None,
                      "kernel_us": kern_us, "kernel_us_from": kern_src,
-                     "algorithmic_bytes": algo_bytes},
+                     "algorithmic_bytes": algo_bytes,
+                     "algorithmic_bytes_with_resample": algo_bytes + resample_bytes},
+        "call_us": call_us,
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_pool,
     }
     print(json.dumps(result), flush=True)
 
@@ -523,11 +554,23 @@ def copy_probe(mib):
 
 
 def cpu_baseline(w, seconds):
-    """The CPU oracle, single-threaded, on consecutive requests of the same
-    workload (whole-call arithmetic per request), for about `seconds`."""
+    """The CPU oracle, single-threaded and pinned to one core, on consecutive
+    requests of the same workload (whole-call arithmetic per request), for
+    about `seconds`."""
     import oracle
     import workloads as W
     oracle.lib()
+    cores = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {cores[0]})
+    try:
+        return _cpu_single(w, seconds)
+    finally:
+        os.sched_setaffinity(0, set(cores))
+
+
+def _cpu_single(w, seconds):
+    import oracle
+    import workloads as W
     t0 = time.perf_counter()
     oracle.verify_workload(W.subset(w, [0]))
     one = max(time.perf_counter() - t0, 1e-6)
@@ -546,8 +589,38 @@ def cpu_baseline(w, seconds):
             "kind": "oracle",
             "requests_per_s": done / el,
             "sample": f"{done} requests of {w.name} in oracle calls of {n} request(s), "
-                      f"{el:.1f}s single-threaded on {platform.processor() or platform.machine()} "
+                      f"{el:.1f}s single-threaded on one core of {platform.processor() or platform.machine()} "
                       f"({os.cpu_count()} cpus visible)"}
+
+
+def cpu_baseline_threads(w, seconds):
+    """The same oracle fanned out over requests on every core this process
+    may use (one thread per core; the oracle's C code runs outside the
+    interpreter lock), for about `seconds`."""
+    import concurrent.futures as cf
+    import oracle
+    import workloads as W
+    oracle.lib()
+    n_thr = max(1, min(len(os.sched_getaffinity(0)), 16, w.B))
+    done = [0] * n_thr
+    t0 = time.perf_counter()
+
+    def worker(k):
+        i = k
+        while time.perf_counter() - t0 < seconds:
+            oracle.verify_workload(W.subset(w, [i % w.B]))
+            done[k] += 1
+            i += n_thr
+
+    with cf.ThreadPoolExecutor(n_thr) as ex:
+        list(ex.map(worker, range(n_thr)))
+    el = time.perf_counter() - t0
+    per_req = w.positions // w.B
+    total = sum(done)
+    return {"value": total * per_req / el, "unit": "positions/s", "cores": n_thr,
+            "kind": "oracle", "requests_per_s": total / el,
+            "sample": f"{total} requests of {w.name}, one request per oracle call, "
+                      f"{el:.1f}s on {n_thr} threads"}
 
 
 if __name__ == "__main__":
