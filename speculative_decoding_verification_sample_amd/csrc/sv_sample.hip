@@ -907,26 +907,28 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     // registers: the logits are read-only for the whole call, and the aligned
     // dword holding the element (same page, so always readable) comes with a
     // scalar load through the constant address space, leaving the vector
-    // queue to the stream; its bits are picked apart after the stream.
+    // queue to the stream; its bits are picked apart after the stream.  The
+    // two dependent scalar loads run once the stream's loads are in flight.
     const int pos = r <= K ? r : r - K - 1;  // position; target row K has no draft token
     bool mine = false, valid = false;
     unsigned mis = 0;
     uint32_t w = 0;
-    if (r != K) {
-      const int x = a.tokens[(size_t)b * K + pos];
-      const int e0 = s * split_elems(DT), e1 = min(V, e0 + split_elems(DT));
-      valid = x >= 0 && x < V;
-      mine = (valid && x >= e0 && x < e1) || (!valid && s == 0);
-      if (mine && valid) {
-        typedef const __attribute__((address_space(4))) uint32_t *const_u32p;
-        const uintptr_t ea = reinterpret_cast<uintptr_t>(rp) + (uintptr_t)x * elem_bytes(DT);
-        mis = (unsigned)(ea & 3u);
-        w = *(const_u32p)(ea - mis);
-      }
-    }
     float M;
     double Z;
-    softmax_tile<DT>(rp, V, s, q.k, &M, &Z);
+    softmax_tile<DT>(rp, V, s, q.k, &M, &Z, [&] {
+      if (r != K) {
+        const int x = a.tokens[(size_t)b * K + pos];
+        const int e0 = s * split_elems(DT), e1 = min(V, e0 + split_elems(DT));
+        valid = x >= 0 && x < V;
+        mine = (valid && x >= e0 && x < e1) || (!valid && s == 0);
+        if (mine && valid) {
+          typedef const __attribute__((address_space(4))) uint32_t *const_u32p;
+          const uintptr_t ea = reinterpret_cast<uintptr_t>(rp) + (uintptr_t)x * elem_bytes(DT);
+          mis = (unsigned)(ea & 3u);
+          w = *(const_u32p)(ea - mis);
+        }
+      }
+    });
     if (threadIdx.x == 0) {
       const size_t g = (size_t)grow * S + s;
       float zh, zl;

@@ -15,10 +15,11 @@ __device__ __forceinline__ u32x4 neg_inf_vec() {
 }
 
 // Softmax statistics of split s of row `rp`: the maximum M and the tempered
-// mass Z = sum 2^((l - M) k), fp32 terms accumulated in fp64.
-template <int DT>
+// mass Z = sum 2^((l - M) k), fp32 terms accumulated in fp64.  `pre` runs
+// once the tile's loads are in flight (work that must not delay them).
+template <int DT, class Pre>
 __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale k, float *M_out,
-                                             double *Z_out) {
+                                             double *Z_out, Pre &&pre) {
   constexpr int EPV = 16 / elem_bytes(DT);
   const Span sp = split_span(rp, V, s, DT);
   const u32x4 *body = span_body(sp, DT);
@@ -32,6 +33,7 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
   }
   const int se = span_scalar_elem(sp, t, DT);
   const float xs = se >= 0 ? load_elem(sp.base, se, DT) : -INFINITY;
+  pre();
 
   float m = xs;
 #pragma unroll
