@@ -26,10 +26,15 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
   const int t = threadIdx.x;
 
   u32x4 buf[kVecPerThread];
+  if (sp.nvec == kThreads * kVecPerThread) {  // a whole split (all but a row's last): no checks
 #pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const int v = t + u * kThreads;
-    buf[u] = v < sp.nvec ? load_stream(body + v) : neg_inf_vec<DT>();
+    for (int u = 0; u < kVecPerThread; ++u) buf[u] = load_stream(body + t + u * kThreads);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const int v = t + u * kThreads;
+      buf[u] = v < sp.nvec ? load_stream(body + v) : neg_inf_vec<DT>();
+    }
   }
   const int se = span_scalar_elem(sp, t, DT);
   const float xs = se >= 0 ? load_elem(sp.base, se, DT) : -INFINITY;
