@@ -108,18 +108,16 @@ __device__ __forceinline__ uint64_t argmax_key(float x, uint32_t idx) {
   return ((uint64_t)key_of_f32(x) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
 }
 
-template <int DT>
-__device__ __forceinline__ uint64_t argmax_tile(const char *rp, int V, int s) {
+// The lane's best key over its part of the split (FULL: a whole split, no
+// bounds checks).
+template <int DT, bool FULL>
+__device__ __forceinline__ uint64_t argmax_lane(const Span &sp, const u32x4 *body, int t) {
   constexpr int EPV = 16 / elem_bytes(DT);
-  const Span sp = split_span(rp, V, s, DT);
-  const u32x4 *body = span_body(sp, DT);
-  const int t = threadIdx.x;
-
   u32x4 buf[kVecPerThread];
 #pragma unroll
   for (int u = 0; u < kVecPerThread; ++u) {
     const int v = t + u * kThreads;
-    buf[u] = v < sp.nvec ? load_stream(body + v) : neg_inf_vec<DT>();
+    buf[u] = (FULL || v < sp.nvec) ? load_stream(body + v) : neg_inf_vec<DT>();
   }
   uint64_t best = 0;
   const int se = span_scalar_elem(sp, t, DT);
@@ -136,7 +134,7 @@ __device__ __forceinline__ uint64_t argmax_tile(const char *rp, int V, int s) {
 #pragma unroll
   for (int u = kVecPerThread - 1; u >= 0; --u) {
     const int v = t + u * kThreads;
-    if (v < sp.nvec) {
+    if (FULL || v < sp.nvec) {
       const int i0 = sp.e0 + sp.head + v * EPV;
 #pragma unroll
       for (int e = EPV - 1; e >= 0; --e) first = vec_elem(buf[u], e, DT) == m ? i0 + e : first;
@@ -146,6 +144,16 @@ __device__ __forceinline__ uint64_t argmax_tile(const char *rp, int V, int s) {
     const uint64_t key = argmax_key(m, (uint32_t)first);
     best = key > best ? key : best;
   }
+  return best;
+}
+
+template <int DT>
+__device__ __forceinline__ uint64_t argmax_tile(const char *rp, int V, int s) {
+  const Span sp = split_span(rp, V, s, DT);
+  const u32x4 *body = span_body(sp, DT);
+  const int t = threadIdx.x;
+  uint64_t best = sp.nvec == kThreads * kVecPerThread ? argmax_lane<DT, true>(sp, body, t)
+                                                      : argmax_lane<DT, false>(sp, body, t);
   __shared__ uint64_t sk[kThreads / 64];
   best = wave_max_u64(best);
   if (lane_id() == 0) sk[t >> 6] = best;
