@@ -73,7 +73,7 @@ struct Decision {
   int mode;             // kModeResidual or kModeBonus
   float m_t, m_d;       // maxima of target row n / draft row n
   float tau_t, tau_d;   // smallest kept logits (-inf: all kept)
-  double inv_t, inv_d;  // 1 / kept mass; inv_d = 0 for the bonus draw (r = p')
+  float inv_t, inv_d;   // 1 / kept mass (the mass is at least 1); inv_d = 0 for the bonus draw (r = p')
 };
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;

@@ -79,15 +79,18 @@ __device__ __forceinline__ double prob_at(float l, float m, float tau, double zk
 // Mass of one token of the drawn row pair: the residual r = max(0, p' - q')
 // (the bonus draw has w_d = 0, so r = p'), or p' itself (P: the fallback when
 // the residual mass is not positive).  Every pass over the pair computes it
-// with this one function, so the values agree bit for bit.
+// with this one function, so the values agree bit for bit.  fp32: the terms
+// 2^((l - m) k) are fp32 values, so a wider product and difference would not
+// make r more accurate than their own rounding (each r within ~2e-7 of p';
+// the sums over a split run in fp64).
 template <bool TOPP, bool P>
 __device__ __forceinline__ double token_mass(float lt, float ld, const Decision &d, Scale k) {
-  double pt = (double)tempered(lt, d.m_t, k) * d.inv_t;
-  if (TOPP) pt = lt >= d.tau_t ? pt : 0.0;
-  if (P) return pt;
-  double qd = (double)tempered(ld, d.m_d, k) * d.inv_d;
-  if (TOPP) qd = ld >= d.tau_d ? qd : 0.0;
-  return fmax(pt - qd, 0.0);
+  float pt = tempered(lt, d.m_t, k) * d.inv_t;
+  if (TOPP) pt = lt >= d.tau_t ? pt : 0.f;
+  if (P) return (double)pt;
+  float qd = tempered(ld, d.m_d, k) * d.inv_d;
+  if (TOPP) qd = ld >= d.tau_d ? qd : 0.f;
+  return (double)fmaxf(pt - qd, 0.f);
 }
 
 __device__ __forceinline__ const char *row_ptr(const void *base, size_t row, int V, int dtype) {
@@ -290,15 +293,15 @@ __device__ __forceinline__ bool decide(const int32_t *tokens, const float *u_acc
       d.mode = n < K ? kModeResidual : kModeBonus;
       d.m_t = L.row_m[n];
       d.tau_t = L.row_tau[n];
-      d.inv_t = 1.0 / L.row_zk[n];
+      d.inv_t = (float)(1.0 / L.row_zk[n]);
       if (n < K) {
         d.m_d = L.row_m[K + 1 + n];
         d.tau_d = L.row_tau[K + 1 + n];
-        d.inv_d = 1.0 / L.row_zk[K + 1 + n];
+        d.inv_d = (float)(1.0 / L.row_zk[K + 1 + n]);
       } else {  // bonus: no draft row; its weight 0 makes the residual p'
         d.m_d = d.m_t;
         d.tau_d = d.tau_t;
-        d.inv_d = 0.0;
+        d.inv_d = 0.f;
       }
       *sd = d;
     }
