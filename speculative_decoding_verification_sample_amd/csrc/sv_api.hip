@@ -167,6 +167,7 @@ int run_sample(const void *target_logits, const void *draft_logits, int dtype,
   a.part_x = carve<sv::u64>(workspace, L.part_x);
   a.rowstat = use_top_p ? carve<sv::RowStat>(workspace, L.rowstat) : nullptr;
   a.rtot = carve<sv::u64>(workspace, L.rtot);
+  a.part_h = use_top_p ? carve<uint16_t>(workspace, L.part_h) : nullptr;
   a.out_accepted = out_accepted;
   a.out_tokens = out_tokens;
   a.out_p = out_p_draft;

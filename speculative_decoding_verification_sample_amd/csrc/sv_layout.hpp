@@ -81,6 +81,12 @@ constexpr int kModeBonus = 1;
 // Largest number of residual splits per row (the draw stages them in LDS).
 constexpr int kMaxSplitsB = 512;
 
+// Top-p: a streaming tile also counts its split's elements by distance from
+// the split maximum on the grid floor(l * k * kHistPerLog2) (1/64 log2 unit,
+// k = log2(e) / T), bins 0 .. kHistBins-1 (24 log2 units), 16-bit counts.
+constexpr int kHistBins = 1536;
+constexpr float kHistPerLog2 = 64.f;
+
 // Arguments of the fused sampling kernel (and what a call shares with the
 // top-p kernel).  temps / topps: per-request temperature and top-p on the
 // device (NULL: the batch-wide k, k64, top_p apply).
@@ -97,6 +103,7 @@ struct SampleArgs {
   u64 *part_m, *part_z, *part_x;
   RowStat *rowstat;
   u64 *rtot;  // per (request, residual split): the split's mass as two tagged fp32 words
+  uint16_t *part_h;  // top-p: per (row, split) kHistBins element counts (null otherwise)
   int32_t *out_accepted, *out_tokens;
   float *out_p, *out_q, *out_mass;
 };
@@ -142,7 +149,7 @@ struct Layout {
   int SB = 0;      // residual splits per row (sampling)
   int rows = 0;    // logit rows streamed
   size_t part_m = 0, part_z = 0, part_x = 0, part_key = 0, part_tag = 0, rowstat = 0;
-  size_t rtot = 0;
+  size_t rtot = 0, part_h = 0;
   // sampling: part_m one self-validating u64 word per (row, split) (the split
   // maximum), part_z two (the split mass as fp32 hi + lo);
   // part_x one word per (request, position, target / draft): the logit of the
@@ -176,6 +183,7 @@ inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p
     L.part_x = take((size_t)B * (size_t)KN * 2 * sizeof(u64));
     L.rowstat = use_top_p ? take((size_t)L.rows * sizeof(RowStat)) : 0;
     L.rtot = take((size_t)B * (size_t)L.SB * 2 * sizeof(u64));
+    L.part_h = use_top_p ? take(cells * kHistBins * sizeof(uint16_t)) : 0;
   } else {
     L.part_key = take(cells * sizeof(uint64_t));
     L.part_tag = take(cells * sizeof(u64));

@@ -148,7 +148,8 @@ __device__ __forceinline__ bool read_cell(const u64 *part_m, const u64 *part_z, 
     const u64 hw = load_agent(&part_z[2 * g]);
     const u64 lw = load_agent(&part_z[2 * g + 1]);
     uint32_t mb, hb, lb;
-    if (unpack_u32(mw, epoch, &mb) & unpack_u32(hw, epoch, &hb) & unpack_u32(lw, epoch, &lb)) {
+    if ((int)unpack_u32(mw, epoch, &mb) & (int)unpack_u32(hw, epoch, &hb) &
+        (int)unpack_u32(lw, epoch, &lb)) {
       *m = __uint_as_float(mb);
       *z = (double)__uint_as_float(hb) + (double)__uint_as_float(lb);
       return true;
@@ -185,7 +186,8 @@ __device__ __forceinline__ bool decide(const int32_t *tokens, const float *u_acc
     got_x = false;
     for (int it = 0; it < kSpinLimit && !got_x; ++it) {
       uint32_t bt, bd;
-      got_x = unpack_u32(load_agent(&px[0]), epoch, &bt) & unpack_u32(load_agent(&px[1]), epoch, &bd);
+      got_x = ((int)unpack_u32(load_agent(&px[0]), epoch, &bt) &
+               (int)unpack_u32(load_agent(&px[1]), epoch, &bd)) != 0;
       lt = __uint_as_float(bt);
       ld = __uint_as_float(bd);
       if (!got_x) spin_pause();
@@ -918,6 +920,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     uint32_t w = 0;
     float M;
     double Z;
+    uint16_t *hist = a.part_h && q.top_p < 1.0 ? a.part_h + ((size_t)grow * S + s) * kHistBins : nullptr;
     softmax_tile<DT>(rp, V, s, q.k, &M, &Z, [&] {
       if (r != K) {
         const int x = a.tokens[(size_t)b * K + pos];
@@ -931,7 +934,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
           w = *(const_u32p)(ea - mis);
         }
       }
-    });
+    }, hist);
     if (threadIdx.x == 0) {
       const size_t g = (size_t)grow * S + s;
       float zh, zl;

@@ -16,14 +16,21 @@ __device__ __forceinline__ u32x4 neg_inf_vec() {
 
 // Softmax statistics of split s of row `rp`: the maximum M and the tempered
 // mass Z = sum 2^((l - M) k), fp32 terms accumulated in fp64.  `pre` runs
-// once the tile's loads are in flight (work that must not delay them).
+// once the tile's loads are in flight (work that must not delay them).  With
+// `hist`, the split's elements are also counted by bin j = floor(M kk) -
+// floor(l kk), kk = k * kHistPerLog2 (bins of 1/64 log2 unit on a grid shared
+// by all splits, so that counts merge across splits by integer offsets);
+// bins past kHistBins are not counted.
 template <int DT, class Pre>
 __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale k, float *M_out,
-                                             double *Z_out, Pre &&pre) {
+                                             double *Z_out, Pre &&pre, uint16_t *hist) {
   constexpr int EPV = 16 / elem_bytes(DT);
   const Span sp = split_span(rp, V, s, DT);
   const u32x4 *body = span_body(sp, DT);
   const int t = threadIdx.x;
+  __shared__ unsigned sh_hist[kHistBins];
+  if (hist)
+    for (int i = t; i < kHistBins; i += kThreads) sh_hist[i] = 0u;
 
   u32x4 buf[kVecPerThread];
   if (sp.nvec == kThreads * kVecPerThread) {  // a whole split (all but a row's last): no checks
@@ -87,6 +94,30 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
     sz[t >> 6] = zz;
   }
   __syncthreads();
+  if (hist) {
+    float M = sm[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, sm[w]);
+    if (M > -INFINITY) {
+      const float kk = (k.hi + k.lo) * kHistPerLog2;
+      const float F = floorf(M * kk);
+      auto count = [&](float x) {
+        if (x > -INFINITY) {
+          const float j = F - floorf(x * kk);  // >= 0: x <= M
+          if (j < (float)kHistBins) atomicAdd(&sh_hist[(int)j], 1u);
+        }
+      };
+#pragma unroll
+      for (int u = 0; u < kVecPerThread; ++u)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) count(vec_elem(buf[u], e, DT));
+      if (se >= 0) count(xs);
+    }
+    __syncthreads();
+    uint32_t *h2 = reinterpret_cast<uint32_t *>(hist);
+    for (int i = t; i < kHistBins / 2; i += kThreads)
+      h2[i] = min(sh_hist[2 * i], 0xFFFFu) | (min(sh_hist[2 * i + 1], 0xFFFFu) << 16);
+  }
   if (t == 0) {
     float M = sm[0];
 #pragma unroll

@@ -5,15 +5,28 @@
 // section "같은 분포를 지키는 작은 장치": temperature / top-p must be applied
 // to both p and q before the test; the nucleus rule itself is the plainest
 // reading, the pages name it only).  With the row maximum M and the
-// normaliser Z known from the streaming pass, one workgroup per row:
-//   1. builds an LDS histogram of tempered mass over bins of the distance
-//      (M - l) * log2(e)/T, 1/8 log2 unit wide (per-wave copies, fp64);
-//      scanning from the nearest bin finds the bin where the cumulative mass
-//      reaches top_p * Z; bins are value intervals, so tie groups never split;
-//   2. resolves the exact cut inside that bin by radix rounds of 8 bits over
-//      order-preserving value keys, again accumulating mass from the top,
-//      until one distinct value remains: that value is tau, the mass at or
-//      above it is the kept mass.
+// normaliser Z known from the streaming pass, one workgroup per row.
+//
+// Usual path, one read of the row: the streaming tiles have counted their
+// elements by distance from the maximum on a shared grid (bins of 1/64
+// log2 unit).  Merged, the counts bound the mass from the top bin by bin
+// (an element of bin J weighs between 2^-(J+phi)/64 and 2^-(J+phi-1)/64),
+// which pins the element where the cumulative mass reaches top_p * Z to a
+// band of bins [b_lo, b_hi]; bins are value intervals, so tie groups never
+// split.  One pass over the row then sums the exact mass of the elements
+// nearer than the band and gathers the band's elements into LDS as
+// order-preserving value keys.  The counts cover 24 log2 units; elements
+// beyond weigh so little that all of them together stay under half of the
+// mass top_p leaves out, so the cut lies within the counted bins.
+//
+// Fallback (a row the counts cannot cover: a small normaliser, a huge logit
+// scale, or no counts): an fp64 LDS histogram of tempered mass over bins of
+// the distance (M - l) * log2(e)/T, 1/8 log2 unit wide, finds the bin where
+// the cumulative mass reaches top_p * Z, and one more pass gathers it.
+//
+// Either way, radix rounds of 8 bits over the gathered keys, accumulating
+// mass from the top, resolve the cut until one distinct value remains:
+// that value is tau, the mass at or above it is the kept mass.
 #include "sv_device.hpp"
 #include "sv_kernels.hpp"
 
@@ -23,13 +36,36 @@ constexpr int kTopThreads = 512;
 constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kBins = 256;
 constexpr float kBinsPerLog2 = 8.f;
-constexpr int kCand = 4096;  // keys of the selected bin held in LDS
+constexpr int kCand = 4096;  // keys of the selected bin or band held in LDS
+// Slack on the count bounds: covers the fp32 rounding of grid positions
+// (|M kk| < 2^18: under 0.03 of a bin, a factor 3.4e-4) and of the masses;
+// a wider slack only widens the band.
+constexpr double kBoundSlack = 1e-3;
 
 namespace {
 
 __device__ __forceinline__ int dist_bin(float x, float M, float kr) {
   const float d = (M - x) * kr;   // >= 0; +inf for x = -inf
   return d < (float)(kBins - 1) ? (int)d : kBins - 1;
+}
+
+// Bin of x on the counting grid, relative to the row maximum's cell F =
+// floor(M kk) (the streaming tiles' grid); kHistBins for -inf or beyond.
+__device__ __forceinline__ int grid_bin(float x, float F, float kk) {
+  if (!(x > -INFINITY)) return kHistBins;
+  const float j = F - floorf(x * kk);
+  return j < (float)kHistBins ? (int)j : kHistBins;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave (fp64, shuffles)
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double u = __shfl_up(v, o, 64);
+    if (l >= o) v += u;
+  }
+  return v;
 }
 
 // Calls f(j, x) for every element of a row: 16-byte vector body, scalar
@@ -87,31 +123,48 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
   const u64 *part_m = a.part_m, *part_z = a.part_z;
   RowStat *rowstat = a.rowstat;
 
-  __shared__ double hist[kTopWaves][kBins];
+  __shared__ double hist[kTopWaves][kBins];  // fallback histogram; the counts share it
+  unsigned *cntf = reinterpret_cast<unsigned *>(&hist[0][0]);
+  static_assert(kHistBins * sizeof(unsigned) <= sizeof(double) * kTopWaves * kBins, "counts fit");
   __shared__ double mass[kBins];
   __shared__ unsigned cnt[kBins], kmin[kBins], kmax[kBins];
+  __shared__ double wsum[2][kTopWaves], wred[kTopWaves];
   __shared__ float sM;
   __shared__ double sZ, s_above;
-  __shared__ int s_bin, s_done;
+  __shared__ int s_bin, s_done, s_fast, s_blo, s_bhi;
   __shared__ unsigned s_prefix;
   __shared__ float s_tau;
   __shared__ double s_kept;
   __shared__ uint32_t cand[kCand];
   __shared__ unsigned s_ncand;
 
-  if (t == 0) {  // the streaming kernel has completed: every partial is in place
+  const float kk = (k.hi + k.lo) * kHistPerLog2;
+  if (t < 64) {  // the streaming kernel has completed: every partial is in place
     const u64 *pm = part_m + (size_t)row * S;
     const u64 *pz = part_z + (size_t)row * S * 2;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, payload_f32(pm[s]));
+    for (int s = t; s < S; s += 64) M = fmaxf(M, payload_f32(pm[s]));
+    M = wave_max(M);
+    M = __shfl(M, 63, 64);
     double Z = 0.0;
-    for (int s = 0; s < S; ++s) {
+    for (int s = t; s < S; s += 64) {
       const float m = payload_f32(pm[s]);
       const double z = (double)payload_f32(pz[2 * s]) + (double)payload_f32(pz[2 * s + 1]);
       if (m > -INFINITY) Z += z * exp2(((double)m - (double)M) * k64);
     }
-    sM = M;
-    sZ = Z;
+    Z = wave_sum(Z);
+    if (t == 63) {
+      sM = M;
+      sZ = Z;
+      // the counts cover the cut when the elements beyond them (each at
+      // most 2^-(kHistBins-1)/64) weigh less than half of (1 - top_p) Z,
+      // and the grid positions are accurate to a small part of a bin
+      s_fast = a.part_h != nullptr && M > -INFINITY && fabsf(M * kk) < 262144.f && top_p < 1.0 &&
+               (double)V * exp2(-(double)(kHistBins - 1) / kHistPerLog2) <= 0.5 * (1.0 - top_p) * Z;
+      s_blo = kHistBins;
+      s_bhi = kHistBins;
+      s_ncand = 0;
+    }
   }
   for (int i = t; i < kTopWaves * kBins; i += kTopThreads) (&hist[0][0])[i] = 0.0;
   __syncthreads();
@@ -130,68 +183,178 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
   }
   const double goal = top_p * Z;
   const float kr = (k.hi + k.lo) * kBinsPerLog2;
+  const bool fast = s_fast;
+  const float F = floorf(M * kk);
+  int sel = -1, blo = 0, bhi = 0;
 
-  // 1. mass by distance bin; the last bin (everything beyond it, where most
-  //    of a long tail sits) is summed in registers instead of LDS atomics
-  {
-    double far = 0.0;
-    for_row<DT>(rp, V, [&](int, float x) {
-      const int bin = dist_bin(x, M, kr);
-      const double tm = (double)tempered(x, M, k);
-      if (bin < kBins - 1)
-        atomicAdd(&hist[w][bin], tm);
-      else
-        far += tm;
-    });
-    far = wave_sum(far);
-    __syncthreads();
-    if ((t & 63) == 0) hist[w][kBins - 1] += far;
-  }
-  __syncthreads();
-  if (t < kBins) {
-    double s = 0.0;
-    for (int u = 0; u < kTopWaves; ++u) s += hist[u][t];
-    mass[t] = s;
-  }
-  __syncthreads();
-  if (t == 0) {
-    double cum = 0.0;
-    int sel = -1;
-    for (int b = 0; b < kBins; ++b) {
-      if (cum + mass[b] >= goal) {
-        sel = b;
-        break;
+  if (fast) {
+    // 1. merge the splits' counts: split s's bin j is the row's bin
+    //    j + floor(M kk) - floor(m_s kk).  Work item i = (split, 8 bins):
+    //    a batch of 16-byte loads is issued before any count is added
+    {
+      const u64 *pm = part_m + (size_t)row * S;
+      const uint16_t *h0 = a.part_h + (size_t)row * S * kHistBins;
+      constexpr int kChunks = kHistBins / 8;  // 16-byte chunks per split
+      const int items = S * kChunks;
+      for (int i0 = t; i0 < items; i0 += 8 * kTopThreads) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * kTopThreads;
+          if (i < items) v[u] = reinterpret_cast<const u32x4 *>(h0)[i];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * kTopThreads;
+          if (i >= items) continue;
+          const int sp = i / kChunks, j0 = (i - sp * kChunks) * 8;
+          const float ms = payload_f32(pm[sp]);
+          if (!(ms > -INFINITY)) continue;
+          const int off = (int)(F - floorf(ms * kk));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const unsigned c = (v[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const int jj = j0 + e + off;
+            if (c && jj < kHistBins) atomicAdd(&cntf[jj], c);
+          }
+        }
       }
-      cum += mass[b];
     }
-    s_bin = sel;
-    s_above = cum;
-    s_prefix = 0;
-    s_done = sel < 0;  // the cumulative mass never reached top_p: keep everything
-    s_tau = -INFINITY;
-    s_kept = cum;
-  }
-  __syncthreads();
-
-  // 2. the selected bin's elements, gathered into LDS as value keys (one
-  //    more pass over the row); if they do not fit, the rounds below read
-  //    the row again each time
-  const int sel = s_bin;
-  if (!s_done) {
-    if (t == 0) s_ncand = 0;
     __syncthreads();
-    for_row<DT>(rp, V, [&](int, float x) {
-      if (dist_bin(x, M, kr) != sel) return;
-      const unsigned slot = atomicAdd(&s_ncand, 1u);
-      if (slot < (unsigned)kCand) cand[slot] = key_of_f32(x);
-    });
+    // 2. running upper / lower bounds of the mass from the top: b_lo = the
+    //    first bin where the upper bound reaches the goal, b_hi = the first
+    //    where the lower bound does
+    {
+      constexpr int kPer = kHistBins / kTopThreads;  // 3 bins per thread
+      const float phi = M * kk - F;                  // in [0, 1)
+      double up[kPer], lo[kPer], su = 0.0, sl = 0.0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int bb = t * kPer + j;
+        const double c = (double)cntf[bb];
+        up[j] = c * (double)exp2f(-((float)bb + phi - 1.f) / kHistPerLog2);
+        lo[j] = c * (double)exp2f(-((float)bb + phi) / kHistPerLog2);
+        su += up[j];
+        sl += lo[j];
+      }
+      const double iu = wave_incl_scan(su), il = wave_incl_scan(sl);
+      if ((t & 63) == 63) {
+        wsum[0][w] = iu;
+        wsum[1][w] = il;
+      }
+      __syncthreads();
+      double cu = iu - su, cl = il - sl;
+      for (int u = 0; u < w; ++u) {
+        cu += wsum[0][u];
+        cl += wsum[1][u];
+      }
+      int bl = kHistBins, bh = kHistBins;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        cu += up[j];
+        cl += lo[j];
+        if (bl == kHistBins && cu * (1.0 + kBoundSlack) >= goal) bl = t * kPer + j;
+        if (bh == kHistBins && cl * (1.0 - kBoundSlack) >= goal) bh = t * kPer + j;
+      }
+      if (bl < kHistBins) atomicMin(&s_blo, bl);
+      if (bh < kHistBins) atomicMin(&s_bhi, bh);
+      __syncthreads();
+      if (t == 0) {
+        s_done = s_blo == kHistBins;  // the bound never reaches top_p: keep everything
+        if (s_bhi == kHistBins) s_bhi = kHistBins - 1;
+        s_prefix = 0;
+        s_tau = -INFINITY;
+        s_kept = Z;
+      }
+      __syncthreads();
+    }
+    // 3. exact mass of the elements nearer than the band; the band's
+    //    elements gathered into LDS as value keys
+    blo = s_blo;
+    bhi = s_bhi;
+    if (!s_done) {
+      double above = 0.0;
+      for_row<DT>(rp, V, [&](int, float x) {
+        const int bin = grid_bin(x, F, kk);
+        if (bin < blo) {
+          above += (double)tempered(x, M, k);
+        } else if (bin <= bhi) {
+          const unsigned slot = atomicAdd(&s_ncand, 1u);
+          if (slot < (unsigned)kCand) cand[slot] = key_of_f32(x);
+        }
+      });
+      above = wave_sum(above);
+      if ((t & 63) == 0) wred[w] = above;
+      __syncthreads();
+      if (t == 0) {
+        double sum = 0.0;
+        for (int u = 0; u < kTopWaves; ++u) sum += wred[u];
+        s_above = sum;
+        s_kept = sum;
+      }
+      __syncthreads();
+    }
+  } else {
+    // fallback 1. mass by distance bin; the last bin (everything beyond
+    //    it, where most of a long tail sits) is summed in registers instead
+    //    of LDS atomics
+    {
+      double far = 0.0;
+      for_row<DT>(rp, V, [&](int, float x) {
+        const int bin = dist_bin(x, M, kr);
+        const double tm = (double)tempered(x, M, k);
+        if (bin < kBins - 1)
+          atomicAdd(&hist[w][bin], tm);
+        else
+          far += tm;
+      });
+      far = wave_sum(far);
+      __syncthreads();
+      if ((t & 63) == 0) hist[w][kBins - 1] += far;
+    }
     __syncthreads();
+    if (t < kBins) {
+      double sum = 0.0;
+      for (int u = 0; u < kTopWaves; ++u) sum += hist[u][t];
+      mass[t] = sum;
+    }
+    __syncthreads();
+    if (t == 0) {
+      double cum = 0.0;
+      int sl = -1;
+      for (int bb = 0; bb < kBins; ++bb) {
+        if (cum + mass[bb] >= goal) {
+          sl = bb;
+          break;
+        }
+        cum += mass[bb];
+      }
+      s_bin = sl;
+      s_above = cum;
+      s_prefix = 0;
+      s_done = sl < 0;  // the cumulative mass never reached top_p: keep everything
+      s_tau = -INFINITY;
+      s_kept = sl < 0 ? Z : cum;
+    }
+    __syncthreads();
+    // fallback 2. the selected bin's elements, gathered into LDS as value
+    //    keys (one more pass over the row)
+    sel = s_bin;
+    if (!s_done) {
+      for_row<DT>(rp, V, [&](int, float x) {
+        if (dist_bin(x, M, kr) != sel) return;
+        const unsigned slot = atomicAdd(&s_ncand, 1u);
+        if (slot < (unsigned)kCand) cand[slot] = key_of_f32(x);
+      });
+      __syncthreads();
+    }
   }
   const unsigned ncand = s_ncand;
   const bool in_lds = ncand <= (unsigned)kCand;
 
-  // 3. exact cut inside the selected bin: radix rounds over value keys,
-  //    accumulating mass from the top
+  // exact cut among the gathered keys (the band, or the selected bin):
+  // radix rounds over value keys, accumulating mass from the top; if they
+  // did not fit in LDS, each round reads the row again
   for (int shift = 24; shift >= 0 && !s_done; shift -= 8) {
     if (t < kBins) {
       mass[t] = 0.0;
@@ -213,7 +376,12 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
       for (unsigned i = t; i < ncand; i += kTopThreads) visit(cand[i]);
     } else {
       for_row<DT>(rp, V, [&](int, float x) {
-        if (dist_bin(x, M, kr) == sel) visit(key_of_f32(x));
+        if (fast) {
+          const int bin = grid_bin(x, F, kk);
+          if (bin >= blo && bin <= bhi) visit(key_of_f32(x));
+        } else if (dist_bin(x, M, kr) == sel) {
+          visit(key_of_f32(x));
+        }
       });
     }
     __syncthreads();
@@ -228,7 +396,7 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
         }
         above += mass[sb];
       }
-      if (pick < 0) {  // rounding: the bin's last group closes the nucleus
+      if (pick < 0) {  // rounding: the last group gathered closes the nucleus
         above = s_above;
         for (int sb = kBins - 1; sb >= 0; --sb) {
           if (!cnt[sb]) continue;
@@ -237,7 +405,7 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
         }
         if (pick >= 0) above -= mass[pick];
       }
-      if (pick < 0) {  // no element in the bin: cannot happen; keep everything
+      if (pick < 0) {  // nothing gathered: cannot happen; keep everything
         s_done = 1;
         s_tau = -INFINITY;
         s_kept = Z;
@@ -258,13 +426,8 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
     RowStat rs;
     rs.m = M;
     rs.z = Z;
-    if (sel < 0) {
-      rs.tau = -INFINITY;
-      rs.zk = Z;
-    } else {
-      rs.tau = s_tau;
-      rs.zk = s_kept;
-    }
+    rs.tau = s_tau;
+    rs.zk = s_kept;
     rowstat[row] = rs;
   }
 }
