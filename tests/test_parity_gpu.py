@@ -143,6 +143,43 @@ def test_topp_with_tie_groups():
             _check(w)
 
 
+def _topp_uses_counts(row, T, top_p, V):
+    """Whether the top-p kernel can take a row's cut from the streaming tiles'
+    counts (the same test the kernel applies, restated in fp64): the logit
+    scale keeps grid positions accurate and the uncounted tail is small."""
+    k = np.log2(np.e) / T
+    x = row.astype(np.float64)
+    M = x.max()
+    Z = np.exp2((x - M) * k).sum()
+    kk = np.float32(k) * np.float32(64.0)
+    return abs(M * kk) < 262144.0 and V * 2.0 ** (-(1536 - 1) / 64.0) <= 0.5 * (1 - top_p) * Z
+
+
+@pytest.mark.parametrize("shift,T,top_p,counts", [
+    (0.0, 0.8, 0.9, True),        # the counts path
+    (1000.0, 0.8, 0.9, True),     # large logits, still within the grid's accuracy
+    (3000.0, 0.8, 0.9, False),    # grid positions too coarse: the two-pass fallback
+    (-3000.0, 0.8, 0.9, False),
+    (0.0, 0.25, 0.999, False),    # a peaked row with top_p near 1: the counts do not reach
+])
+def test_topp_count_path_and_fallback(shift, T, top_p, counts):
+    """The top-p threshold from merged per-split counts and from the fp64
+    two-pass fallback, each against the oracle; shifting every logit by a
+    constant leaves the distributions unchanged but moves the grid."""
+    rng = np.random.default_rng(int(abs(shift)) + int(1000 * T))
+    B, K, V = 4, 3, 40009
+    t32 = (rng.normal(0, 2.5, (B, K + 1, V)) + shift).astype(np.float32)
+    d32 = (t32[:, :K] + rng.normal(0, 1, (B, K, V))).astype(np.float32)
+    tp = float(np.float32(top_p))
+    assert all(_topp_uses_counts(t32[b, i], T, tp, V) == counts
+               for b in range(B) for i in range(K + 1))
+    toks = W.drafter_tokens(d32, T, tp, rng)
+    w = W.Workload("sample", f"top-p shift={shift} T={T} p={top_p}", B, K, V, "f32", t32, d32,
+                   toks, W.uniforms_on_grid(rng, (B, K)), W.uniforms_on_grid(rng, (B,)),
+                   float(np.float32(T)), tp)
+    _check(w)
+
+
 def test_flat_rows_and_neg_inf():
     rng = np.random.default_rng(4)
     B, K, V = 4, 3, 3000
