@@ -86,6 +86,19 @@ constexpr int kMaxSplitsB = 512;
 // k = log2(e) / T), bins 0 .. kHistBins-1 (24 log2 units), 16-bit counts.
 constexpr int kHistBins = 1536;
 constexpr float kHistPerLog2 = 64.f;
+// Top-p: keys of a row's band kept for the cut (more: the cut reads the row).
+constexpr int kBandKeys = 4096;
+
+// Top-p, per row, from the band kernel to the gather and cut kernels.
+struct TopBand {
+  double z;       // sum over the row of 2^((l - m) k)
+  float m;        // row maximum
+  int state;      // kTopDone (RowStat written), kTopCounts (band valid), kTopFallback
+  int blo, bhi;   // the band of count bins that holds the cut
+};
+constexpr int kTopDone = 0;
+constexpr int kTopCounts = 1;
+constexpr int kTopFallback = 2;
 
 // Arguments of the fused sampling kernel (and what a call shares with the
 // top-p kernel).  temps / topps: per-request temperature and top-p on the
@@ -104,6 +117,10 @@ struct SampleArgs {
   RowStat *rowstat;
   u64 *rtot;  // per (request, residual split): the split's mass as two tagged fp32 words
   uint16_t *part_h;  // top-p: per (row, split) kHistBins element counts (null otherwise)
+  TopBand *topband;  // top-p: per row
+  unsigned *band_n;  // top-p: per row, keys gathered so far
+  uint32_t *band_keys;  // top-p: per row, kBandKeys keys
+  double *band_above;   // top-p: per (row, split), exact mass above the band
   int32_t *out_accepted, *out_tokens;
   float *out_p, *out_q, *out_mass;
 };
@@ -149,7 +166,7 @@ struct Layout {
   int SB = 0;      // residual splits per row (sampling)
   int rows = 0;    // logit rows streamed
   size_t part_m = 0, part_z = 0, part_x = 0, part_key = 0, part_tag = 0, rowstat = 0;
-  size_t rtot = 0, part_h = 0;
+  size_t rtot = 0, part_h = 0, topband = 0, band_n = 0, band_keys = 0, band_above = 0;
   // sampling: part_m one self-validating u64 word per (row, split) (the split
   // maximum), part_z two (the split mass as fp32 hi + lo);
   // part_x one word per (request, position, target / draft): the logit of the
@@ -183,7 +200,13 @@ inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p
     L.part_x = take((size_t)B * (size_t)KN * 2 * sizeof(u64));
     L.rowstat = use_top_p ? take((size_t)L.rows * sizeof(RowStat)) : 0;
     L.rtot = take((size_t)B * (size_t)L.SB * 2 * sizeof(u64));
-    L.part_h = use_top_p ? take(cells * kHistBins * sizeof(uint16_t)) : 0;
+    if (use_top_p) {
+      L.part_h = take(cells * kHistBins * sizeof(uint16_t));
+      L.topband = take((size_t)L.rows * sizeof(TopBand));
+      L.band_n = take((size_t)L.rows * sizeof(unsigned));
+      L.band_keys = take((size_t)L.rows * kBandKeys * sizeof(uint32_t));
+      L.band_above = take(cells * sizeof(double));
+    }
   } else {
     L.part_key = take(cells * sizeof(uint64_t));
     L.part_tag = take(cells * sizeof(u64));

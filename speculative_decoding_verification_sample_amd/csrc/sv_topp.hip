@@ -4,31 +4,31 @@
 // mass first reaches top_p of the row, and renormalise (ariser.io review,
 // section "같은 분포를 지키는 작은 장치": temperature / top-p must be applied
 // to both p and q before the test; the nucleus rule itself is the plainest
-// reading, the pages name it only).  With the row maximum M and the
-// normaliser Z known from the streaming pass, one workgroup per row.
-//
-// Usual path, one read of the row: the streaming tiles have counted their
-// elements by distance from the maximum on a shared grid (bins of 1/64
-// log2 unit).  Merged, the counts bound the mass from the top bin by bin
-// (an element of bin J weighs between 2^-(J+phi)/64 and 2^-(J+phi-1)/64),
-// which pins the element where the cumulative mass reaches top_p * Z to a
-// band of bins [b_lo, b_hi]; bins are value intervals, so tie groups never
-// split.  One pass over the row then sums the exact mass of the elements
-// nearer than the band and gathers the band's elements into LDS as
-// order-preserving value keys.  The counts cover 24 log2 units; elements
-// beyond weigh so little that all of them together stay under half of the
-// mass top_p leaves out, so the cut lies within the counted bins.
-//
-// Fallback (a row the counts cannot cover: a small normaliser, a huge logit
-// scale, or no counts): an fp64 LDS histogram of tempered mass over bins of
-// the distance (M - l) * log2(e)/T, 1/8 log2 unit wide, finds the bin where
-// the cumulative mass reaches top_p * Z, and one more pass gathers it.
-//
-// Either way, radix rounds of 8 bits over the gathered keys, accumulating
-// mass from the top, resolve the cut until one distinct value remains:
-// that value is tau, the mass at or above it is the kept mass.
+// reading, the pages name it only).  The streaming pass has left each
+// row's maximum M, normaliser Z and, per split, counts of its elements by
+// distance from the maximum on a shared grid (bins of 1/64 log2 unit).
+// Three launches:
+//   band (one workgroup per row): merge the counts; an element of bin J
+//     weighs between 2^-(J+phi)/64 and 2^-(J+phi-1)/64, so running bounds
+//     of the mass from the top pin the element where the cumulative mass
+//     reaches top_p * Z to a band of bins [b_lo, b_hi] (bins are value
+//     intervals: tie groups never split).  The counts cover 24 log2 units;
+//     the elements beyond weigh so little that all of them together stay
+//     under half of the mass top_p leaves out, so the cut lies inside.
+//   gather (one workgroup per row split, the streaming tiles' geometry):
+//     the exact mass of the split's elements nearer than the band, and the
+//     band's elements as order-preserving value keys in a per-row list.
+//   cut (one workgroup per row): radix rounds of 8 bits over the keys,
+//     accumulating mass from the top, until one distinct value remains:
+//     that value is tau, the mass at or above it is the kept mass.
+// A row the counts cannot cover (a small normaliser, a huge logit scale)
+// takes the fallback in the cut launch: an fp64 LDS histogram of tempered
+// mass over bins of the distance (M - l) * log2(e)/T, 1/8 log2 unit wide,
+// finds the bin where the cumulative mass reaches top_p * Z, one more pass
+// gathers that bin, and the same radix rounds finish.
 #include "sv_device.hpp"
 #include "sv_kernels.hpp"
+#include "sv_tiles.hpp"
 
 namespace sv {
 
@@ -103,45 +103,60 @@ __device__ __forceinline__ void for_row(const char *row, int V, F &&f) {
   }
 }
 
+
+// The row's place in the call and its request's sampling parameters.
+struct TopRow {
+  const char *rp;
+  ReqParams q;
+};
+template <int DT>
+__device__ __forceinline__ TopRow top_row(const SampleArgs &a, int row) {
+  const int rows_t = a.B * (a.K + 1);
+  const size_t row_bytes = (size_t)a.V * elem_bytes(DT);
+  TopRow r;
+  r.rp = row < rows_t ? a.target + (size_t)row * row_bytes
+                      : a.draft + (size_t)(row - rows_t) * row_bytes;
+  const int b = row < rows_t ? row / (a.K + 1) : (row - rows_t) / a.K;
+  r.q = request_params(a.temps, a.topps, a.k64, a.k, a.top_p, b);
+  return r;
+}
+
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// band: per row, M and Z from the streaming partials, then the counts
+// ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
+__global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int w = t >> 6;
   const int V = a.V, S = a.S;
-  const int rows_t = a.B * (a.K + 1);
-  const size_t row_bytes = (size_t)V * elem_bytes(DT);
-  const char *rp = row < rows_t ? a.target + (size_t)row * row_bytes
-                                : a.draft + (size_t)(row - rows_t) * row_bytes;
-  const int b = row < rows_t ? row / (a.K + 1) : (row - rows_t) / a.K;
-  const ReqParams q = request_params(a.temps, a.topps, a.k64, a.k, a.top_p, b);
-  if (q.invalid || q.greedy) return;  // no softmax statistics for this request
-  const Scale k = q.k;
-  const double k64 = q.k64, top_p = q.top_p;
-  const u64 *part_m = a.part_m, *part_z = a.part_z;
-  RowStat *rowstat = a.rowstat;
-
-  __shared__ double hist[kTopWaves][kBins];  // fallback histogram; the counts share it
-  unsigned *cntf = reinterpret_cast<unsigned *>(&hist[0][0]);
-  static_assert(kHistBins * sizeof(unsigned) <= sizeof(double) * kTopWaves * kBins, "counts fit");
-  __shared__ double mass[kBins];
-  __shared__ unsigned cnt[kBins], kmin[kBins], kmax[kBins];
-  __shared__ double wsum[2][kTopWaves], wred[kTopWaves];
-  __shared__ float sM;
-  __shared__ double sZ, s_above;
-  __shared__ int s_bin, s_done, s_fast, s_blo, s_bhi;
-  __shared__ unsigned s_prefix;
-  __shared__ float s_tau;
-  __shared__ double s_kept;
-  __shared__ uint32_t cand[kCand];
-  __shared__ unsigned s_ncand;
-
+  const TopRow tr = top_row<DT>(a, row);
+  if (tr.q.invalid || tr.q.greedy) {  // no softmax statistics for this request
+    if (t == 0) {
+      TopBand tb;
+      tb.z = 0.0;
+      tb.m = -INFINITY;
+      tb.state = kTopDone;
+      tb.blo = tb.bhi = 0;
+      a.topband[row] = tb;
+    }
+    return;
+  }
+  const Scale k = tr.q.k;
+  const double k64 = tr.q.k64, top_p = tr.q.top_p;
+  const u64 *pm = a.part_m + (size_t)row * S;
+  const u64 *pz = a.part_z + (size_t)row * S * 2;
   const float kk = (k.hi + k.lo) * kHistPerLog2;
+
+  __shared__ unsigned cntf[kHistBins];
+  __shared__ double wsum[2][kTopWaves];
+  __shared__ float sM;
+  __shared__ double sZ;
+  __shared__ int s_fast, s_blo, s_bhi;
+
   if (t < 64) {  // the streaming kernel has completed: every partial is in place
-    const u64 *pm = part_m + (size_t)row * S;
-    const u64 *pz = part_z + (size_t)row * S * 2;
     float M = -INFINITY;
     for (int s = t; s < S; s += 64) M = fmaxf(M, payload_f32(pm[s]));
     M = wave_max(M);
@@ -159,14 +174,13 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
       // the counts cover the cut when the elements beyond them (each at
       // most 2^-(kHistBins-1)/64) weigh less than half of (1 - top_p) Z,
       // and the grid positions are accurate to a small part of a bin
-      s_fast = a.part_h != nullptr && M > -INFINITY && fabsf(M * kk) < 262144.f && top_p < 1.0 &&
+      s_fast = M > -INFINITY && fabsf(M * kk) < 262144.f && top_p < 1.0 &&
                (double)V * exp2(-(double)(kHistBins - 1) / kHistPerLog2) <= 0.5 * (1.0 - top_p) * Z;
       s_blo = kHistBins;
       s_bhi = kHistBins;
-      s_ncand = 0;
     }
   }
-  for (int i = t; i < kTopWaves * kBins; i += kTopThreads) (&hist[0][0])[i] = 0.0;
+  for (int i = t; i < kHistBins; i += kTopThreads) cntf[i] = 0u;
   __syncthreads();
   const float M = sM;
   const double Z = sZ;
@@ -177,124 +191,281 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
       rs.z = Z;
       rs.tau = -INFINITY;
       rs.zk = Z;
-      rowstat[row] = rs;
+      a.rowstat[row] = rs;
+      TopBand tb;
+      tb.z = Z;
+      tb.m = M;
+      tb.state = kTopDone;
+      tb.blo = tb.bhi = 0;
+      a.topband[row] = tb;
+    }
+    return;
+  }
+  if (!s_fast) {
+    if (t == 0) {
+      TopBand tb;
+      tb.z = Z;
+      tb.m = M;
+      tb.state = kTopFallback;
+      tb.blo = tb.bhi = 0;
+      a.topband[row] = tb;
     }
     return;
   }
   const double goal = top_p * Z;
-  const float kr = (k.hi + k.lo) * kBinsPerLog2;
-  const bool fast = s_fast;
   const float F = floorf(M * kk);
-  int sel = -1, blo = 0, bhi = 0;
 
-  if (fast) {
-    // 1. merge the splits' counts: split s's bin j is the row's bin
-    //    j + floor(M kk) - floor(m_s kk).  Work item i = (split, 8 bins):
-    //    a batch of 16-byte loads is issued before any count is added
-    {
-      const u64 *pm = part_m + (size_t)row * S;
-      const uint16_t *h0 = a.part_h + (size_t)row * S * kHistBins;
-      constexpr int kChunks = kHistBins / 8;  // 16-byte chunks per split
-      const int items = S * kChunks;
-      for (int i0 = t; i0 < items; i0 += 8 * kTopThreads) {
-        u32x4 v[8];
+  // merge the splits' counts: split s's bin j is the row's bin j + floor(M
+  // kk) - floor(m_s kk).  Work item i = (split, 8 bins): a batch of 16-byte
+  // loads is issued before any count is added.
+  {
+    const uint16_t *h0 = a.part_h + (size_t)row * S * kHistBins;
+    constexpr int kChunks = kHistBins / 8;  // 16-byte chunks per split
+    const int items = S * kChunks;
+    for (int i0 = t; i0 < items; i0 += 8 * kTopThreads) {
+      u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = i0 + u * kTopThreads;
-          if (i < items) v[u] = reinterpret_cast<const u32x4 *>(h0)[i];
-        }
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kTopThreads;
+        if (i < items) v[u] = reinterpret_cast<const u32x4 *>(h0)[i];
+      }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = i0 + u * kTopThreads;
-          if (i >= items) continue;
-          const int sp = i / kChunks, j0 = (i - sp * kChunks) * 8;
-          const float ms = payload_f32(pm[sp]);
-          if (!(ms > -INFINITY)) continue;
-          const int off = (int)(F - floorf(ms * kk));
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kTopThreads;
+        if (i >= items) continue;
+        const int sp = i / kChunks, j0 = (i - sp * kChunks) * 8;
+        const float ms = payload_f32(pm[sp]);
+        if (!(ms > -INFINITY)) continue;
+        const int off = (int)(F - floorf(ms * kk));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const unsigned c = (v[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            const int jj = j0 + e + off;
-            if (c && jj < kHistBins) atomicAdd(&cntf[jj], c);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const unsigned c = (v[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          const int jj = j0 + e + off;
+          if (c && jj < kHistBins) atomicAdd(&cntf[jj], c);
         }
       }
+    }
+  }
+  __syncthreads();
+  // running upper / lower bounds of the mass from the top: b_lo = the first
+  // bin where the upper bound reaches the goal, b_hi = the first where the
+  // lower bound does
+  {
+    constexpr int kPer = kHistBins / kTopThreads;  // 3 bins per thread
+    const float phi = M * kk - F;                  // in [0, 1)
+    double up[kPer], lo[kPer], su = 0.0, sl = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int bb = t * kPer + j;
+      const double c = (double)cntf[bb];
+      up[j] = c * (double)exp2f(-((float)bb + phi - 1.f) / kHistPerLog2);
+      lo[j] = c * (double)exp2f(-((float)bb + phi) / kHistPerLog2);
+      su += up[j];
+      sl += lo[j];
+    }
+    const double iu = wave_incl_scan(su), il = wave_incl_scan(sl);
+    if ((t & 63) == 63) {
+      wsum[0][w] = iu;
+      wsum[1][w] = il;
     }
     __syncthreads();
-    // 2. running upper / lower bounds of the mass from the top: b_lo = the
-    //    first bin where the upper bound reaches the goal, b_hi = the first
-    //    where the lower bound does
-    {
-      constexpr int kPer = kHistBins / kTopThreads;  // 3 bins per thread
-      const float phi = M * kk - F;                  // in [0, 1)
-      double up[kPer], lo[kPer], su = 0.0, sl = 0.0;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int bb = t * kPer + j;
-        const double c = (double)cntf[bb];
-        up[j] = c * (double)exp2f(-((float)bb + phi - 1.f) / kHistPerLog2);
-        lo[j] = c * (double)exp2f(-((float)bb + phi) / kHistPerLog2);
-        su += up[j];
-        sl += lo[j];
-      }
-      const double iu = wave_incl_scan(su), il = wave_incl_scan(sl);
-      if ((t & 63) == 63) {
-        wsum[0][w] = iu;
-        wsum[1][w] = il;
-      }
-      __syncthreads();
-      double cu = iu - su, cl = il - sl;
-      for (int u = 0; u < w; ++u) {
-        cu += wsum[0][u];
-        cl += wsum[1][u];
-      }
-      int bl = kHistBins, bh = kHistBins;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        cu += up[j];
-        cl += lo[j];
-        if (bl == kHistBins && cu * (1.0 + kBoundSlack) >= goal) bl = t * kPer + j;
-        if (bh == kHistBins && cl * (1.0 - kBoundSlack) >= goal) bh = t * kPer + j;
-      }
-      if (bl < kHistBins) atomicMin(&s_blo, bl);
-      if (bh < kHistBins) atomicMin(&s_bhi, bh);
-      __syncthreads();
-      if (t == 0) {
-        s_done = s_blo == kHistBins;  // the bound never reaches top_p: keep everything
-        if (s_bhi == kHistBins) s_bhi = kHistBins - 1;
-        s_prefix = 0;
-        s_tau = -INFINITY;
-        s_kept = Z;
-      }
-      __syncthreads();
+    double cu = iu - su, cl = il - sl;
+    for (int u = 0; u < w; ++u) {
+      cu += wsum[0][u];
+      cl += wsum[1][u];
     }
-    // 3. exact mass of the elements nearer than the band; the band's
-    //    elements gathered into LDS as value keys
-    blo = s_blo;
-    bhi = s_bhi;
-    if (!s_done) {
-      double above = 0.0;
-      for_row<DT>(rp, V, [&](int, float x) {
-        const int bin = grid_bin(x, F, kk);
-        if (bin < blo) {
-          above += (double)tempered(x, M, k);
-        } else if (bin <= bhi) {
-          const unsigned slot = atomicAdd(&s_ncand, 1u);
-          if (slot < (unsigned)kCand) cand[slot] = key_of_f32(x);
-        }
-      });
-      above = wave_sum(above);
-      if ((t & 63) == 0) wred[w] = above;
-      __syncthreads();
-      if (t == 0) {
-        double sum = 0.0;
-        for (int u = 0; u < kTopWaves; ++u) sum += wred[u];
+    int bl = kHistBins, bh = kHistBins;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      cu += up[j];
+      cl += lo[j];
+      if (bl == kHistBins && cu * (1.0 + kBoundSlack) >= goal) bl = t * kPer + j;
+      if (bh == kHistBins && cl * (1.0 - kBoundSlack) >= goal) bh = t * kPer + j;
+    }
+    if (bl < kHistBins) atomicMin(&s_blo, bl);
+    if (bh < kHistBins) atomicMin(&s_bhi, bh);
+  }
+  __syncthreads();
+  if (t == 0) {
+    TopBand tb;
+    tb.z = Z;
+    tb.m = M;
+    // the bound never reaching top_p would mean the counts missed mass:
+    // the fallback decides such a row
+    tb.state = s_blo == kHistBins ? kTopFallback : kTopCounts;
+    tb.blo = s_blo;
+    tb.bhi = s_bhi == kHistBins ? kHistBins - 1 : s_bhi;
+    a.topband[row] = tb;
+    a.band_n[row] = 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gather: per row split, the exact mass above the band and the band's keys
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_topp_gather(SampleArgs a) {
+  const int S = a.S;
+  const int row = blockIdx.x / S, s = blockIdx.x - row * S;
+  const int t = threadIdx.x;
+  const TopRow tr = top_row<DT>(a, row);
+  if (tr.q.invalid || tr.q.greedy || !(tr.q.top_p < 1.0)) return;
+  const Scale k = tr.q.k;
+  const float kk = (k.hi + k.lo) * kHistPerLog2;
+  constexpr int EPV = 16 / elem_bytes(DT);
+  const Span sp = split_span(tr.rp, a.V, s, DT);
+  const u32x4 *body = span_body(sp, DT);
+
+  u32x4 buf[kVecPerThread];
+  if (sp.nvec == kThreads * kVecPerThread) {
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) buf[u] = load_stream(body + t + u * kThreads);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      const int v = t + u * kThreads;
+      buf[u] = v < sp.nvec ? load_stream(body + v) : neg_inf_vec<DT>();
+    }
+  }
+  const int se = span_scalar_elem(sp, t, DT);
+  const float xs = se >= 0 ? load_elem(sp.base, se, DT) : -INFINITY;
+  // the row's band, read while the split's loads are in flight (a row the
+  // counts did not cover is decided by the cut launch)
+  const TopBand tb = a.topband[row];
+  if (tb.state != kTopCounts) return;
+  const float M = tb.m, F = floorf(M * kk);
+  const int blo = tb.blo, bhi = tb.bhi;
+
+  // the lane's mass above the band, and how many of its elements lie in it.
+  // With y = x kk (the product grid_bin floors): bin < blo iff y >= F - blo
+  // + 1, bin <= bhi iff y >= F - bhi (integers, exact in fp32 below 2^24),
+  // so an element far below the band costs one product and one compare.
+  const float ya = F - (float)blo + 1.f, yb = F - (float)bhi;
+  double above = 0.0;
+  int nb = 0;
+  auto visit = [&](float x) {
+    const float y = x * kk;
+    if (y >= yb) {
+      if (y >= ya) above += (double)tempered(x, M, k);
+      else ++nb;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) visit(vec_elem(buf[u], e, DT));
+  visit(xs);
+
+  // workgroup prefix of the band counts (wave scans, then the wave totals)
+  __shared__ int wtot[kThreads / 64];
+  __shared__ double wabove[kThreads / 64];
+  __shared__ unsigned s_base;
+  int incl = nb;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if ((t & 63) >= o) incl += u;
+  }
+  const double wa = wave_sum(above);
+  if ((t & 63) == 63) {
+    wtot[t >> 6] = incl;
+    wabove[t >> 6] = wa;
+  }
+  __syncthreads();
+  int before = incl - nb, total = 0;
+#pragma unroll
+  for (int u = 0; u < kThreads / 64; ++u) {
+    if (u < (t >> 6)) before += wtot[u];
+    total += wtot[u];
+  }
+  if (t == 0) {
+    double sum = 0.0;
+#pragma unroll
+    for (int u = 0; u < kThreads / 64; ++u) sum += wabove[u];
+    a.band_above[(size_t)row * S + s] = sum;
+    s_base = total > 0 ? atomicAdd(&a.band_n[row], (unsigned)total) : 0u;
+  }
+  __syncthreads();
+  if (nb == 0) return;
+  // the lane's band keys into the row's list, at its place in the tile's run
+  uint32_t *keys = a.band_keys + (size_t)row * kBandKeys;
+  unsigned slot = s_base + (unsigned)before;
+  auto put = [&](float x) {
+    const float y = x * kk;
+    if (y >= yb && y < ya) {
+      if (slot < (unsigned)kBandKeys) keys[slot] = key_of_f32(x);
+      ++slot;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u)
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) put(vec_elem(buf[u], e, DT));
+  put(xs);
+}
+
+// ---------------------------------------------------------------------------
+// cut: per row, the radix rounds (and the fallback for uncovered rows)
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
+  const int row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int w = t >> 6;
+  const int V = a.V, S = a.S;
+  const TopRow tr = top_row<DT>(a, row);
+  if (tr.q.invalid || tr.q.greedy) return;
+  const TopBand tb = a.topband[row];
+  if (tb.state == kTopDone) return;
+  const char *rp = tr.rp;
+  const Scale k = tr.q.k;
+  const double top_p = tr.q.top_p;
+  const float M = tb.m;
+  const double Z = tb.z;
+  const double goal = top_p * Z;
+  const float kk = (k.hi + k.lo) * kHistPerLog2;
+  const float kr = (k.hi + k.lo) * kBinsPerLog2;
+  const bool fast = tb.state == kTopCounts;
+  const float F = floorf(M * kk);
+  const int blo = tb.blo, bhi = tb.bhi;
+
+  __shared__ double hist[kTopWaves][kBins];
+  __shared__ double mass[kBins];
+  __shared__ unsigned cnt[kBins], kmin[kBins], kmax[kBins];
+  __shared__ double s_above;
+  __shared__ int s_bin, s_done;
+  __shared__ unsigned s_prefix;
+  __shared__ float s_tau;
+  __shared__ double s_kept;
+  __shared__ uint32_t cand[kCand];
+  __shared__ unsigned s_ncand;
+  int sel = -1;
+
+  if (fast) {
+    // the band's keys and the exact mass above them, from the gather tiles
+    const unsigned n = a.band_n[row];
+    if (t < 64) {
+      double sum = 0.0;
+      for (int s = t; s < S; s += 64) sum += a.band_above[(size_t)row * S + s];
+      sum = wave_sum(sum);
+      if (t == 63) {
         s_above = sum;
         s_kept = sum;
+        s_done = 0;
+        s_prefix = 0;
+        s_tau = -INFINITY;
+        s_ncand = n;
       }
-      __syncthreads();
     }
+    if (n <= (unsigned)kCand) {
+      const uint32_t *keys = a.band_keys + (size_t)row * kBandKeys;
+      for (unsigned i = t; i < n; i += kTopThreads) cand[i] = keys[i];
+    }
+    __syncthreads();
   } else {
+    if (t == 0) s_ncand = 0;
+    for (int i = t; i < kTopWaves * kBins; i += kTopThreads) (&hist[0][0])[i] = 0.0;
+    __syncthreads();
     // fallback 1. mass by distance bin; the last bin (everything beyond
     //    it, where most of a long tail sits) is summed in registers instead
     //    of LDS atomics
@@ -355,12 +526,18 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
   // exact cut among the gathered keys (the band, or the selected bin):
   // radix rounds over value keys, accumulating mass from the top; if they
   // did not fit in LDS, each round reads the row again
+  __shared__ double exc[kBins], rtot[kBins / 64];
+  __shared__ int s_first, s_lastnz;
   for (int shift = 24; shift >= 0 && !s_done; shift -= 8) {
     if (t < kBins) {
       mass[t] = 0.0;
       cnt[t] = 0;
       kmin[t] = 0xFFFFFFFFu;
       kmax[t] = 0u;
+    }
+    if (t == 0) {
+      s_first = kBins;
+      s_lastnz = -1;
     }
     __syncthreads();
     const unsigned prefix = s_prefix;
@@ -385,39 +562,44 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
       });
     }
     __syncthreads();
+    // from the top bin down (lane t: bin 255 - t), the mass of the
+    // non-empty bins above each one; the pick is the first non-empty bin
+    // where the mass so far reaches the goal (if rounding leaves none, the
+    // last non-empty bin closes the nucleus)
+    double v = 0.0;
+    bool nz = false;
+    if (t < kBins) {
+      nz = cnt[kBins - 1 - t] != 0u;
+      v = nz ? mass[kBins - 1 - t] : 0.0;
+    }
+    const double incl = wave_incl_scan(v);
+    if (t < kBins && (t & 63) == 63) rtot[t >> 6] = incl;
+    __syncthreads();
+    if (t < kBins) {
+      double ex = incl - v;
+      for (int u = 0; u < (t >> 6); ++u) ex += rtot[u];
+      exc[t] = ex;
+      if (nz && s_above + ex + v >= goal) atomicMin(&s_first, t);
+      if (nz) atomicMax(&s_lastnz, t);
+    }
+    __syncthreads();
     if (t == 0) {
-      double above = s_above;
-      int pick = -1;
-      for (int sb = kBins - 1; sb >= 0; --sb) {
-        if (!cnt[sb]) continue;
-        if (above + mass[sb] >= goal) {
-          pick = sb;
-          break;
-        }
-        above += mass[sb];
-      }
-      if (pick < 0) {  // rounding: the last group gathered closes the nucleus
-        above = s_above;
-        for (int sb = kBins - 1; sb >= 0; --sb) {
-          if (!cnt[sb]) continue;
-          pick = sb;
-          above += mass[sb];
-        }
-        if (pick >= 0) above -= mass[pick];
-      }
-      if (pick < 0) {  // nothing gathered: cannot happen; keep everything
+      const int pt = s_first < kBins ? s_first : s_lastnz;
+      if (pt < 0) {  // nothing gathered: cannot happen; keep everything
         s_done = 1;
         s_tau = -INFINITY;
         s_kept = Z;
         s_above = 0.0;
       } else {
-      s_above = above;
-      s_prefix = (prefix << 8) | (unsigned)pick;
-      if (kmin[pick] == kmax[pick] || shift == 0) {
-        s_done = 1;
-        s_tau = f32_of_key(kmin[pick]);
-        s_kept = above + mass[pick];
-      }
+        const int pick = kBins - 1 - pt;
+        const double above = s_above + exc[pt];
+        s_above = above;
+        s_prefix = (prefix << 8) | (unsigned)pick;
+        if (kmin[pick] == kmax[pick] || shift == 0) {
+          s_done = 1;
+          s_tau = f32_of_key(kmin[pick]);
+          s_kept = above + mass[pick];
+        }
       }
     }
     __syncthreads();
@@ -428,16 +610,21 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_select(SampleArgs a) {
     rs.z = Z;
     rs.tau = s_tau;
     rs.zk = s_kept;
-    rowstat[row] = rs;
+    a.rowstat[row] = rs;
   }
 }
 
 hipError_t launch_topp_select(const SampleArgs &a, int dtype, hipStream_t stream) {
-  dim3 grid(a.B * (2 * a.K + 1)), block(kTopThreads);
-  if (dtype == kBF16)
-    hipLaunchKernelGGL(k_topp_select<kBF16>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_topp_select<kF32>, grid, block, 0, stream, a);
+  const int rows = a.B * (2 * a.K + 1);
+  if (dtype == kBF16) {
+    hipLaunchKernelGGL(k_topp_band<kBF16>, dim3(rows), dim3(kTopThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_topp_gather<kBF16>, dim3(rows * a.S), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_topp_cut<kBF16>, dim3(rows), dim3(kTopThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(k_topp_band<kF32>, dim3(rows), dim3(kTopThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_topp_gather<kF32>, dim3(rows * a.S), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_topp_cut<kF32>, dim3(rows), dim3(kTopThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
