@@ -123,7 +123,7 @@ def main():
         copy_probe(args.copy_probe_mib)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: this benchmark runs on one GPU only (--gpus {args.gpus} requested); "
               "the verify step shards over requests with no exchange, see the design notes.",
               file=sys.stderr)
         sys.exit(2)
