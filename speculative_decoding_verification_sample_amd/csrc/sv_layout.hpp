@@ -83,9 +83,11 @@ constexpr int kMaxSplitsB = 512;
 
 // Top-p: a streaming tile also counts its split's elements by distance from
 // the split maximum on the grid floor(l * k * kHistPerLog2) (1/64 log2 unit,
-// k = log2(e) / T), bins 0 .. kHistBins-1 (24 log2 units), 16-bit counts.
+// k = log2(e) / T), bins 0 .. kHistBins-1 (24 log2 units), 8-bit counts
+// that stop at kCountSat (a saturated bin sends its row to the fallback).
 constexpr int kHistBins = 1536;
 constexpr float kHistPerLog2 = 64.f;
+constexpr unsigned kCountSat = 255u;
 // Top-p: keys of a row's band kept for the cut (more: the cut reads the row).
 constexpr int kBandKeys = 4096;
 
@@ -116,7 +118,7 @@ struct SampleArgs {
   u64 *part_m, *part_z, *part_x;
   RowStat *rowstat;
   u64 *rtot;  // per (request, residual split): the split's mass as two tagged fp32 words
-  uint16_t *part_h;  // top-p: per (row, split) kHistBins element counts (null otherwise)
+  uint8_t *part_h;  // top-p: per (row, split) kHistBins element counts (null otherwise)
   TopBand *topband;  // top-p: per row
   unsigned *band_n;  // top-p: per row, keys gathered so far
   uint32_t *band_keys;  // top-p: per row, kBandKeys keys
@@ -201,7 +203,7 @@ inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p
     L.rowstat = use_top_p ? take((size_t)L.rows * sizeof(RowStat)) : 0;
     L.rtot = take((size_t)B * (size_t)L.SB * 2 * sizeof(u64));
     if (use_top_p) {
-      L.part_h = take(cells * kHistBins * sizeof(uint16_t));
+      L.part_h = take(cells * kHistBins * sizeof(uint8_t));
       L.topband = take((size_t)L.rows * sizeof(TopBand));
       L.band_n = take((size_t)L.rows * sizeof(unsigned));
       L.band_keys = take((size_t)L.rows * kBandKeys * sizeof(uint32_t));

@@ -920,7 +920,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     uint32_t w = 0;
     float M;
     double Z;
-    uint16_t *hist = a.part_h && q.top_p < 1.0 ? a.part_h + ((size_t)grow * S + s) * kHistBins : nullptr;
+    uint8_t *hist = a.part_h && q.top_p < 1.0 ? a.part_h + ((size_t)grow * S + s) * kHistBins : nullptr;
     softmax_tile<DT>(rp, V, s, q.k, &M, &Z, [&] {
       if (r != K) {
         const int x = a.tokens[(size_t)b * K + pos];

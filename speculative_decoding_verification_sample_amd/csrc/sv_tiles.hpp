@@ -23,12 +23,12 @@ __device__ __forceinline__ u32x4 neg_inf_vec() {
 // bins past kHistBins are not counted.
 template <int DT, class Pre>
 __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale k, float *M_out,
-                                             double *Z_out, Pre &&pre, uint16_t *hist) {
+                                             double *Z_out, Pre &&pre, uint8_t *hist) {
   constexpr int EPV = 16 / elem_bytes(DT);
   const Span sp = split_span(rp, V, s, DT);
   const u32x4 *body = span_body(sp, DT);
   const int t = threadIdx.x;
-  __shared__ unsigned sh_hist[kHistBins];
+  __shared__ unsigned sh_hist[kHistBins + 64];  // + one spare slot per lane (not written out)
   if (hist)
     for (int i = t; i < kHistBins; i += kThreads) sh_hist[i] = 0u;
 
@@ -101,11 +101,12 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
     if (M > -INFINITY) {
       const float kk = (k.hi + k.lo) * kHistPerLog2;
       const float F = floorf(M * kk);
+      // branch-free: an element past the counted bins (or -inf) adds to
+      // its lane's spare slot instead (distinct per lane: no conflicts)
+      const int spare = kHistBins + lane_id();
       auto count = [&](float x) {
-        if (x > -INFINITY) {
-          const float j = F - floorf(x * kk);  // >= 0: x <= M
-          if (j < (float)kHistBins) atomicAdd(&sh_hist[(int)j], 1u);
-        }
+        const float j = F - floorf(x * kk);  // >= 0: x <= M; +inf for x = -inf
+        atomicAdd(&sh_hist[j < (float)kHistBins ? (int)j : spare], 1u);
       };
 #pragma unroll
       for (int u = 0; u < kVecPerThread; ++u)
@@ -114,9 +115,10 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
       if (se >= 0) count(xs);
     }
     __syncthreads();
-    uint32_t *h2 = reinterpret_cast<uint32_t *>(hist);
-    for (int i = t; i < kHistBins / 2; i += kThreads)
-      h2[i] = min(sh_hist[2 * i], 0xFFFFu) | (min(sh_hist[2 * i + 1], 0xFFFFu) << 16);
+    uint32_t *h4 = reinterpret_cast<uint32_t *>(hist);
+    for (int i = t; i < kHistBins / 4; i += kThreads)
+      h4[i] = min(sh_hist[4 * i], kCountSat) | (min(sh_hist[4 * i + 1], kCountSat) << 8) |
+              (min(sh_hist[4 * i + 2], kCountSat) << 16) | (min(sh_hist[4 * i + 3], kCountSat) << 24);
   }
   if (t == 0) {
     float M = sm[0];

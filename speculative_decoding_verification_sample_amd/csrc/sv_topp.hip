@@ -216,11 +216,16 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
   const float F = floorf(M * kk);
 
   // merge the splits' counts: split s's bin j is the row's bin j + floor(M
-  // kk) - floor(m_s kk).  Work item i = (split, 8 bins): a batch of 16-byte
-  // loads is issued before any count is added.
+  // kk) - floor(m_s kk).  Work item i = (split, 16 bins): a batch of
+  // 16-byte loads is issued before any count is added.  A saturated count
+  // (some bin of a split holds more than kCountSat elements) leaves the row
+  // to the fallback.
+  __shared__ int s_sat;
+  if (t == 0) s_sat = 0;
+  __syncthreads();
   {
-    const uint16_t *h0 = a.part_h + (size_t)row * S * kHistBins;
-    constexpr int kChunks = kHistBins / 8;  // 16-byte chunks per split
+    const uint8_t *h0 = a.part_h + (size_t)row * S * kHistBins;
+    constexpr int kChunks = kHistBins / 16;  // 16-byte chunks per split
     const int items = S * kChunks;
     for (int i0 = t; i0 < items; i0 += 8 * kTopThreads) {
       u32x4 v[8];
@@ -233,15 +238,16 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
       for (int u = 0; u < 8; ++u) {
         const int i = i0 + u * kTopThreads;
         if (i >= items) continue;
-        const int sp = i / kChunks, j0 = (i - sp * kChunks) * 8;
+        const int sp = i / kChunks, j0 = (i - sp * kChunks) * 16;
         const float ms = payload_f32(pm[sp]);
         if (!(ms > -INFINITY)) continue;
         const int off = (int)(F - floorf(ms * kk));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const unsigned c = (v[u][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        for (int e = 0; e < 16; ++e) {
+          const unsigned c = (v[u][e >> 2] >> (8 * (e & 3))) & 0xFFu;
           const int jj = j0 + e + off;
           if (c && jj < kHistBins) atomicAdd(&cntf[jj], c);
+          if (c == kCountSat) s_sat = 1;
         }
       }
     }
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
     tb.m = M;
     // the bound never reaching top_p would mean the counts missed mass:
     // the fallback decides such a row
-    tb.state = s_blo == kHistBins ? kTopFallback : kTopCounts;
+    tb.state = s_blo == kHistBins || s_sat ? kTopFallback : kTopCounts;
     tb.blo = s_blo;
     tb.bhi = s_bhi == kHistBins ? kHistBins - 1 : s_bhi;
     a.topband[row] = tb;
