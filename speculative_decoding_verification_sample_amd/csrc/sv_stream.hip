@@ -20,12 +20,17 @@ namespace sv {
 
 namespace {
 
+// A row's top choice from its splits' keys; the keys are loaded eight at a
+// time, all issued before any is compared (one round trip per eight).
 __device__ __forceinline__ int combine_argmax(const uint64_t *part_key, size_t row, int S) {
   const uint64_t *pk = part_key + row * (size_t)S;
   uint64_t best = 0;
-  for (int s = 0; s < S; ++s) {
-    const uint64_t v = load_agent(&pk[s]);
-    best = v > best ? v : best;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = s0 + u < S ? load_agent(&pk[s0 + u]) : 0ull;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) best = v[u] > best ? v[u] : best;
   }
   return (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFull));
 }
