@@ -37,15 +37,14 @@ __global__ __launch_bounds__(kThreads) void k_kv_commit(
 
   __shared__ int s_node[64];
   __shared__ int s_ok;
+  // the path's node ids are loaded with its length, not after it (a lane
+  // past the path ignores what it read)
+  const int raw = path_nodes && t >= 1 && t <= N ? path_nodes[(size_t)b * N + t - 1] : t;
   const int c = cache_len[b];
   const int d = path_len[b];
   const bool dok = d >= 0 && d <= N - 1 && c >= 0 && (long)c + N <= S;
   if (t == 0) s_ok = dok;
-  if (t < 64) {
-    int node = -1;
-    if (dok && t <= d) node = t == 0 ? 0 : (path_nodes ? path_nodes[(size_t)b * N + t - 1] : t);
-    s_node[t] = node;
-  }
+  if (t < 64) s_node[t] = dok && t <= d ? (t == 0 ? 0 : raw) : -1;
   __syncthreads();
   // nodes strictly increasing, within the cycle's slots
   if (dok && t >= 1 && t <= d && (s_node[t] <= s_node[t - 1] || s_node[t] > N - 1)) s_ok = 0;
