@@ -126,6 +126,14 @@ __device__ __forceinline__ float f32_of_key(uint32_t k) {
 
 __device__ __forceinline__ float exp2_fast(float a) { return __builtin_amdgcn_exp2f(a); }
 
+// The upper 16 bits of x's fp32 pattern, raised by one unit where that is
+// needed for the value they denote (low bits zero) not to lie below x:
+// positive x with nonzero low bits.  Any pattern for NaN.
+__device__ __forceinline__ uint32_t f32_hi_up(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b >> 16) + ((b >> 31) == 0u && (b & 0xFFFFu) != 0u ? 1u : 0u);
+}
+
 __device__ __forceinline__ float tempered(float l, float m, Scale k) {
   float d = l - m;
   return exp2_fast(fmaf(d, k.hi, d * k.lo));

@@ -934,7 +934,7 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
           w = *(const_u32p)(ea - mis);
         }
       }
-    }, hist);
+    }, hist, hist ? a.part_c + ((size_t)grow * S + s) * kChunksPerSplit : nullptr);
     if (threadIdx.x == 0) {
       const size_t g = (size_t)grow * S + s;
       float zh, zl;

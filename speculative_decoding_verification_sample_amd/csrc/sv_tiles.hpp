@@ -20,10 +20,12 @@ __device__ __forceinline__ u32x4 neg_inf_vec() {
 // `hist`, the split's elements are also counted by bin j = floor(M kk) -
 // floor(l kk), kk = k * kHistPerLog2 (bins of 1/64 log2 unit on a grid shared
 // by all splits, so that counts merge across splits by integer offsets);
-// bins past kHistBins are not counted.
+// bins past kHistBins are not counted.  With `hist`, `cmax` takes the
+// split's chunk maxima (kChunksPerSplit entries, f32_hi_up of each).
 template <int DT, class Pre>
 __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale k, float *M_out,
-                                             double *Z_out, Pre &&pre, uint8_t *hist) {
+                                             double *Z_out, Pre &&pre, uint8_t *hist,
+                                             uint16_t *cmax) {
   constexpr int EPV = 16 / elem_bytes(DT);
   const Span sp = split_span(rp, V, s, DT);
   const u32x4 *body = span_body(sp, DT);
@@ -95,6 +97,21 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
   }
   __syncthreads();
   if (hist) {
+    // chunk maxima: the lane's elements of slot u, then its group of eight
+    // lanes (quad moves, then the half-row mirror); lane t keeps slot t % 8
+    const uint32_t ninf = __float_as_uint(-INFINITY);
+    uint32_t mine = 0;
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u) {
+      float c = vec_elem(buf[u], 0, DT);
+#pragma unroll
+      for (int e = 1; e < EPV; ++e) c = fmaxf(c, vec_elem(buf[u], e, DT));
+      c = fmaxf(c, __uint_as_float(dpp_u32<kDppXor1>(ninf, __float_as_uint(c))));
+      c = fmaxf(c, __uint_as_float(dpp_u32<kDppXor2>(ninf, __float_as_uint(c))));
+      c = fmaxf(c, __uint_as_float(dpp_u32<kDppHalfMirror>(ninf, __float_as_uint(c))));
+      mine = (t & (kChunkLanes - 1)) == u ? f32_hi_up(c) : mine;
+    }
+    cmax[t] = (uint16_t)mine;
     float M = sm[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, sm[w]);

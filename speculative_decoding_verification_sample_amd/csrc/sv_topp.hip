@@ -15,9 +15,10 @@
 //     intervals: tie groups never split).  The counts cover 24 log2 units;
 //     the elements beyond weigh so little that all of them together stay
 //     under half of the mass top_p leaves out, so the cut lies inside.
-//   gather (one workgroup per row split, the streaming tiles' geometry):
-//     the exact mass of the split's elements nearer than the band, and the
-//     band's elements as order-preserving value keys in a per-row list.
+//   gather (one workgroup per row): the exact mass of the row's elements
+//     nearer than the band, and the band's elements as order-preserving
+//     value keys in a per-row list; the streaming pass's chunk maxima let
+//     it read only the 128-byte lines that can hold such elements.
 //   cut (one workgroup per row): radix rounds of 8 bits over the keys,
 //     accumulating mass from the top, until one distinct value remains:
 //     that value is tau, the mass at or above it is the kept mass.
@@ -302,112 +303,189 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
     tb.blo = s_blo;
     tb.bhi = s_bhi == kHistBins ? kHistBins - 1 : s_bhi;
     a.topband[row] = tb;
-    a.band_n[row] = 0u;
   }
 }
 
 // ---------------------------------------------------------------------------
-// gather: per row split, the exact mass above the band and the band's keys
+// gather: per row, the exact mass above the band and the band's keys
 // ---------------------------------------------------------------------------
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_topp_gather(SampleArgs a) {
-  const int S = a.S;
-  const int row = blockIdx.x / S, s = blockIdx.x - row * S;
-  const int t = threadIdx.x;
-  const TopRow tr = top_row<DT>(a, row);
-  if (tr.q.invalid || tr.q.greedy || !(tr.q.top_p < 1.0)) return;
-  const Scale k = tr.q.k;
-  const float kk = (k.hi + k.lo) * kHistPerLog2;
-  constexpr int EPV = 16 / elem_bytes(DT);
-  const Span sp = split_span(tr.rp, a.V, s, DT);
-  const u32x4 *body = span_body(sp, DT);
+constexpr int kGWin = kTopThreads / 16;             // splits per window (16 lanes a split's scalars)
+constexpr int kGWinEnt = kGWin * kChunksPerSplit;   // chunk entries per window
+constexpr int kGRounds = kGWinEnt / (8 * kTopThreads);  // 16-byte loads of entries per lane
+constexpr int kGSlots = 8;                          // chunk lines per lane group and pass
+constexpr int kGPerPass = kTopThreads / kChunkLanes * kGSlots;
 
-  u32x4 buf[kVecPerThread];
-  if (sp.nvec == kThreads * kVecPerThread) {
-#pragma unroll
-    for (int u = 0; u < kVecPerThread; ++u) buf[u] = load_stream(body + t + u * kThreads);
-  } else {
-#pragma unroll
-    for (int u = 0; u < kVecPerThread; ++u) {
-      const int v = t + u * kThreads;
-      buf[u] = v < sp.nvec ? load_stream(body + v) : neg_inf_vec<DT>();
-    }
-  }
-  const int se = span_scalar_elem(sp, t, DT);
-  const float xs = se >= 0 ? load_elem(sp.base, se, DT) : -INFINITY;
-  // the row's band, read while the split's loads are in flight (a row the
-  // counts did not cover is decided by the cut launch)
-  const TopBand tb = a.topband[row];
-  if (tb.state != kTopCounts) return;
-  const float M = tb.m, F = floorf(M * kk);
-  const int blo = tb.blo, bhi = tb.bhi;
-
-  // the lane's mass above the band, and how many of its elements lie in it.
-  // With y = x kk (the product grid_bin floors): bin < blo iff y >= F - blo
-  // + 1, bin <= bhi iff y >= F - bhi (integers, exact in fp32 below 2^24),
-  // so an element far below the band costs one product and one compare.
-  const float ya = F - (float)blo + 1.f, yb = F - (float)bhi;
-  double above = 0.0;
-  int nb = 0;
-  auto visit = [&](float x) {
-    const float y = x * kk;
-    if (y >= yb) {
-      if (y >= ya) above += (double)tempered(x, M, k);
-      else ++nb;
-    }
-  };
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u)
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) visit(vec_elem(buf[u], e, DT));
-  visit(xs);
-
-  // workgroup prefix of the band counts (wave scans, then the wave totals)
-  __shared__ int wtot[kThreads / 64];
-  __shared__ double wabove[kThreads / 64];
-  __shared__ unsigned s_base;
-  int incl = nb;
+// Exclusive prefix of v over the workgroup; *total gets the sum.  Whole
+// workgroup; wtot is free again on return.
+__device__ __forceinline__ int block_excl_scan(int v, int *wtot, int *total) {
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  int incl = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int u = __shfl_up(incl, o, 64);
-    if ((t & 63) >= o) incl += u;
+    if (l >= o) incl += u;
   }
-  const double wa = wave_sum(above);
-  if ((t & 63) == 63) {
-    wtot[t >> 6] = incl;
-    wabove[t >> 6] = wa;
+  if (l == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = incl - v, sum = 0;
+#pragma unroll
+  for (int u = 0; u < kTopWaves; ++u) {
+    if (u < w) before += wtot[u];
+    sum += wtot[u];
   }
   __syncthreads();
-  int before = incl - nb, total = 0;
+  *total = sum;
+  return before;
+}
+
+// One workgroup per row, over windows of kGWin splits: the window's chunk
+// maxima pick the 128-byte lines that can hold an element at or above the
+// band (a chunk whose rounded-up maximum c has c kk < F - bhi holds none:
+// x <= c and kk > 0 give x kk <= c kk, rounding keeps the order); their
+// indices are packed into LDS, and passes of kGPerPass lines, each line read
+// by a group of eight lanes, visit only those.  Every split's scalar head
+// and tail elements are visited too.  The row's keys go to its list at
+// offsets from a workgroup scan, with no atomics.
+template <int DT>
+__global__ __launch_bounds__(kTopThreads) void k_topp_gather(SampleArgs a) {
+  const int row = blockIdx.x, S = a.S, t = threadIdx.x;
+  const TopRow tr = top_row<DT>(a, row);
+  if (tr.q.invalid || tr.q.greedy || !(tr.q.top_p < 1.0)) return;
+  // a row the counts did not cover is decided by the cut launch
+  const TopBand tb = a.topband[row];
+  if (tb.state != kTopCounts) return;
+  const Scale k = tr.q.k;
+  const float kk = (k.hi + k.lo) * kHistPerLog2;
+  const float M = tb.m, F = floorf(M * kk);
+  constexpr int EPV = 16 / elem_bytes(DT);
+  static_assert(2 * (EPV - 1) <= 16, "a split's scalars fit its 16 lanes");
+  // With y = x kk (the product grid_bin floors): bin < blo iff y >= F - blo
+  // + 1, bin <= bhi iff y >= F - bhi (integers, exact in fp32 below 2^24),
+  // so an element below the band costs one product and one compare.
+  const float ya = F - (float)tb.blo + 1.f, yb = F - (float)tb.bhi;
+
+  __shared__ uint16_t list[kGWinEnt];
+  __shared__ int wtot[kTopWaves];
+  __shared__ double wsum[kTopWaves];
+  uint32_t *keys = a.band_keys + (size_t)row * kBandKeys;
+  const uint16_t *cm = a.part_c + (size_t)row * S * kChunksPerSplit;
+  double above = 0.0;
+  int kbase = 0;  // keys of the passes before (uniform)
+  // split bodies: splits start 32 KB apart, so every full split has the
+  // first one's head and vector count; the last has its own count
+  const Span sp0 = split_span(tr.rp, a.V, 0, DT), spl = split_span(tr.rp, a.V, S - 1, DT);
+  const u32x4 *body0 = span_body(sp0, DT);
+  constexpr int kSplitVecs = kThreads * kVecPerThread;
+
+  for (int s0 = 0; s0 < S; s0 += kGWin) {
+    const int sw = min(kGWin, S - s0), nent = sw * kChunksPerSplit;
+    // the window's chunk maxima, eight entries a lane and round ...
+    u32x4 cw[kGRounds];
 #pragma unroll
-  for (int u = 0; u < kThreads / 64; ++u) {
-    if (u < (t >> 6)) before += wtot[u];
-    total += wtot[u];
+    for (int r = 0; r < kGRounds; ++r) {
+      const int e = (r * kTopThreads + t) * 8;
+      cw[r] = e < nent ? *reinterpret_cast<const u32x4 *>(cm + (size_t)s0 * kChunksPerSplit + e)
+                       : neg_inf_vec<kBF16>();
+    }
+    // ... and each split's scalars (lanes 16 j .. 16 j + 15 for split s0 + j)
+    float xs = -INFINITY;
+    {
+      const int j = t >> 4, q = t & 15;
+      if (j < sw) {
+        const Span sp = split_span(tr.rp, a.V, s0 + j, DT);
+        const int se = span_scalar_elem(sp, q, DT);
+        if (se >= 0) xs = load_elem(sp.base, se, DT);
+      }
+    }
+    // the needed entries, packed into the list
+    uint32_t bits[kGRounds];
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kGRounds; ++r) {
+      bits[r] = 0u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t h = (cw[r][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+        bits[r] |= !(__uint_as_float(h << 16) * kk < yb) ? 1u << j : 0u;
+      }
+      cnt += __builtin_popcount(bits[r]);
+    }
+    int n;
+    int pos = block_excl_scan(cnt, wtot, &n);
+#pragma unroll
+    for (int r = 0; r < kGRounds; ++r) {
+      const int e0 = (r * kTopThreads + t) * 8;
+      for (uint32_t b = bits[r]; b; b &= b - 1u) list[pos++] = (uint16_t)(e0 + __builtin_ctz(b));
+    }
+    __syncthreads();
+
+    // passes over the listed lines: lane group t / 8 takes items t / 8 +
+    // 64 r, lane t one 16-byte vector of each (entry g * 8 + u of a split
+    // is its vectors 8 g .. 8 g + 7 of slot u: v = 8 g + lane + u kThreads)
+    for (int p0 = 0; p0 == 0 || p0 < n; p0 += kGPerPass) {
+      // every list read first, then every load
+      int ent[kGSlots];
+#pragma unroll
+      for (int r = 0; r < kGSlots; ++r) {
+        const int i = p0 + r * (kTopThreads / kChunkLanes) + t / kChunkLanes;
+        ent[r] = i < n ? (int)list[i] : -1;
+      }
+      u32x4 buf[kGSlots];
+#pragma unroll
+      for (int r = 0; r < kGSlots; ++r) {
+        buf[r] = neg_inf_vec<DT>();
+        if (ent[r] >= 0) {
+          const int sp = s0 + ent[r] / kChunksPerSplit, e = ent[r] % kChunksPerSplit;
+          const int v = (e / kVecPerThread) * kChunkLanes + (t % kChunkLanes) + (e % kVecPerThread) * kThreads;
+          if (v < (sp == S - 1 ? spl.nvec : sp0.nvec))
+            buf[r] = load_stream(body0 + (size_t)sp * kSplitVecs + v);
+        }
+      }
+      const float xp = p0 == 0 ? xs : -INFINITY;
+      int nb = 0;
+      auto visit = [&](float x) {
+        const float y = x * kk;
+        if (y >= yb) {
+          if (y >= ya) above += (double)tempered(x, M, k);
+          else ++nb;
+        }
+      };
+#pragma unroll
+      for (int r = 0; r < kGSlots; ++r)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) visit(vec_elem(buf[r], e, DT));
+      visit(xp);
+      int tot;
+      const int before = block_excl_scan(nb, wtot, &tot);
+      if (nb) {
+        unsigned slot = (unsigned)(kbase + before);
+        auto put = [&](float x) {
+          const float y = x * kk;
+          if (y >= yb && y < ya) {
+            if (slot < (unsigned)kBandKeys) keys[slot] = key_of_f32(x);
+            ++slot;
+          }
+        };
+#pragma unroll
+        for (int r = 0; r < kGSlots; ++r)
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) put(vec_elem(buf[r], e, DT));
+        put(xp);
+      }
+      kbase += tot;
+    }
+    __syncthreads();  // the list and split table are rewritten by the next window
   }
+  const double wa = wave_sum(above);
+  if ((t & 63) == 0) wsum[t >> 6] = wa;
+  __syncthreads();
   if (t == 0) {
     double sum = 0.0;
 #pragma unroll
-    for (int u = 0; u < kThreads / 64; ++u) sum += wabove[u];
-    a.band_above[(size_t)row * S + s] = sum;
-    s_base = total > 0 ? atomicAdd(&a.band_n[row], (unsigned)total) : 0u;
+    for (int u = 0; u < kTopWaves; ++u) sum += wsum[u];
+    a.band_above[row] = sum;
+    a.band_n[row] = (unsigned)kbase;
   }
-  __syncthreads();
-  if (nb == 0) return;
-  // the lane's band keys into the row's list, at its place in the tile's run
-  uint32_t *keys = a.band_keys + (size_t)row * kBandKeys;
-  unsigned slot = s_base + (unsigned)before;
-  auto put = [&](float x) {
-    const float y = x * kk;
-    if (y >= yb && y < ya) {
-      if (slot < (unsigned)kBandKeys) keys[slot] = key_of_f32(x);
-      ++slot;
-    }
-  };
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u)
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) put(vec_elem(buf[u], e, DT));
-  put(xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -418,7 +496,7 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int w = t >> 6;
-  const int V = a.V, S = a.S;
+  const int V = a.V;
   const TopRow tr = top_row<DT>(a, row);
   if (tr.q.invalid || tr.q.greedy) return;
   const TopBand tb = a.topband[row];
@@ -450,18 +528,14 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
   if (fast) {
     // the band's keys and the exact mass above them, from the gather tiles
     const unsigned n = a.band_n[row];
-    if (t < 64) {
-      double sum = 0.0;
-      for (int s = t; s < S; s += 64) sum += a.band_above[(size_t)row * S + s];
-      sum = wave_sum(sum);
-      if (t == 63) {
-        s_above = sum;
-        s_kept = sum;
-        s_done = 0;
-        s_prefix = 0;
-        s_tau = -INFINITY;
-        s_ncand = n;
-      }
+    if (t == 0) {
+      const double sum = a.band_above[row];
+      s_above = sum;
+      s_kept = sum;
+      s_done = 0;
+      s_prefix = 0;
+      s_tau = -INFINITY;
+      s_ncand = n;
     }
     if (n <= (unsigned)kCand) {
       const uint32_t *keys = a.band_keys + (size_t)row * kBandKeys;
@@ -624,11 +698,11 @@ hipError_t launch_topp_select(const SampleArgs &a, int dtype, hipStream_t stream
   const int rows = a.B * (2 * a.K + 1);
   if (dtype == kBF16) {
     hipLaunchKernelGGL(k_topp_band<kBF16>, dim3(rows), dim3(kTopThreads), 0, stream, a);
-    hipLaunchKernelGGL(k_topp_gather<kBF16>, dim3(rows * a.S), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_topp_gather<kBF16>, dim3(rows), dim3(kTopThreads), 0, stream, a);
     hipLaunchKernelGGL(k_topp_cut<kBF16>, dim3(rows), dim3(kTopThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL(k_topp_band<kF32>, dim3(rows), dim3(kTopThreads), 0, stream, a);
-    hipLaunchKernelGGL(k_topp_gather<kF32>, dim3(rows * a.S), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_topp_gather<kF32>, dim3(rows), dim3(kTopThreads), 0, stream, a);
     hipLaunchKernelGGL(k_topp_cut<kF32>, dim3(rows), dim3(kTopThreads), 0, stream, a);
   }
   return hipGetLastError();
