@@ -128,9 +128,10 @@ __device__ __forceinline__ float exp2_fast(float a) { return __builtin_amdgcn_ex
 
 // The upper 16 bits of x's fp32 pattern, raised by one unit where that is
 // needed for the value they denote (low bits zero) not to lie below x:
-// positive x with nonzero low bits.  Any pattern for NaN.
+// positive x with nonzero low bits.  NaN gives +inf.
 __device__ __forceinline__ uint32_t f32_hi_up(float x) {
   const uint32_t b = __float_as_uint(x);
+  if (x != x) return 0x7F80u;
   return (b >> 16) + ((b >> 31) == 0u && (b & 0xFFFFu) != 0u ? 1u : 0u);
 }
 

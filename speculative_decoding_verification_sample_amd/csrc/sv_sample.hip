@@ -818,7 +818,7 @@ __device__ __forceinline__ void greedy_in_sample(const SampleArgs &a, int b) {
 // MIXED: per-request parameters (temps / topps on the device); otherwise the
 // batch-wide ones and no greedy requests (the per-request code stays out of
 // the batch-wide kernel, where it would cost registers and issue slots).
-template <int DT, bool MIXED>
+template <int DT, bool MIXED, bool TOPP>
 __global__ __launch_bounds__(kThreads) void k_sample_fused(
     const char *__restrict__ target, const char *__restrict__ draft,
     const int32_t *__restrict__ tokens, const float *__restrict__ u_accept,
@@ -920,8 +920,8 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
     uint32_t w = 0;
     float M;
     double Z;
-    uint8_t *hist = a.part_h && q.top_p < 1.0 ? a.part_h + ((size_t)grow * S + s) * kHistBins : nullptr;
-    softmax_tile<DT>(rp, V, s, q.k, &M, &Z, [&] {
+    uint8_t *hist = TOPP && a.part_h && q.top_p < 1.0 ? a.part_h + ((size_t)grow * S + s) * kHistBins : nullptr;
+    softmax_tile<DT, TOPP>(rp, V, s, q.k, &M, &Z, [&] {
       if (r != K) {
         const int x = a.tokens[(size_t)b * K + pos];
         const int e0 = s * split_elems(DT), e1 = min(V, e0 + split_elems(DT));
@@ -976,8 +976,13 @@ hipError_t launch_sample(const SampleArgs &args, int dtype, hipStream_t stream) 
   const int blocks = a.phase == 0 ? nA + nB : a.phase == 1 ? nA : nB;
   a.lag = std::max(1, std::min(a.lag, a.B));
   const bool mixed = a.temps != nullptr || a.topps != nullptr;
-  auto kern = dtype == kBF16 ? (mixed ? k_sample_fused<kBF16, true> : k_sample_fused<kBF16, false>)
-                             : (mixed ? k_sample_fused<kF32, true> : k_sample_fused<kF32, false>);
+  // the streaming tiles of a top-p call also count and record chunk maxima
+  const bool topp = a.part_h != nullptr && a.phase == 1;
+  auto kern = dtype == kBF16
+                  ? (mixed ? (topp ? k_sample_fused<kBF16, true, true> : k_sample_fused<kBF16, true, false>)
+                           : (topp ? k_sample_fused<kBF16, false, true> : k_sample_fused<kBF16, false, false>))
+                  : (mixed ? (topp ? k_sample_fused<kF32, true, true> : k_sample_fused<kF32, true, false>)
+                           : (topp ? k_sample_fused<kF32, false, true> : k_sample_fused<kF32, false, false>));
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kThreads), 0, stream, a.target, a.draft, a.tokens,
                      a.u_accept, a.u_sample, a.temps, a.topps, a.part_m, a.part_z, a.part_x,
                      a.rowstat, a.rtot, a.out_accepted, a.out_tokens, a.out_p, a.out_q,
@@ -994,8 +999,8 @@ int resident_workgroups(int dtype) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 2048;
-    const void *fn = d ? (const void *)k_sample_fused<kBF16, false>
-                       : (const void *)k_sample_fused<kF32, false>;
+    const void *fn = d ? (const void *)k_sample_fused<kBF16, false, false>
+                       : (const void *)k_sample_fused<kF32, false, false>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess)
       per_cu = 4;
     cache[d] = std::max(1, cus * per_cu);

@@ -21,8 +21,9 @@ __device__ __forceinline__ u32x4 neg_inf_vec() {
 // floor(l kk), kk = k * kHistPerLog2 (bins of 1/64 log2 unit on a grid shared
 // by all splits, so that counts merge across splits by integer offsets);
 // bins past kHistBins are not counted.  With `hist`, `cmax` takes the
-// split's chunk maxima (kChunksPerSplit entries, f32_hi_up of each).
-template <int DT, class Pre>
+// split's chunk maxima (kChunksPerSplit entries, f32_hi_up of each).  HIST
+// false compiles neither (both pointers are then ignored).
+template <int DT, bool HIST, class Pre>
 __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale k, float *M_out,
                                              double *Z_out, Pre &&pre, uint8_t *hist,
                                              uint16_t *cmax) {
@@ -50,10 +51,21 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
   pre();
 
   float m = xs;
+  float mu[kVecPerThread];  // HIST: each slot's maximum over the lane's elements
+  if constexpr (HIST) {
 #pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u)
+    for (int u = 0; u < kVecPerThread; ++u) {
+      mu[u] = vec_elem(buf[u], 0, DT);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) m = fmaxf(m, vec_elem(buf[u], e, DT));
+      for (int e = 1; e < EPV; ++e) mu[u] = fmaxf(mu[u], vec_elem(buf[u], e, DT));
+      m = fmaxf(m, mu[u]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kVecPerThread; ++u)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) m = fmaxf(m, vec_elem(buf[u], e, DT));
+  }
 
   // 2^((l - m) k) with k = hi + lo: the exponent is taken as
   // (l hi + c) + l lo with c = -m hi rounded to a float (two fused
@@ -96,22 +108,28 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
     sz[t >> 6] = zz;
   }
   __syncthreads();
-  if (hist) {
-    // chunk maxima: the lane's elements of slot u, then its group of eight
-    // lanes (quad moves, then the half-row mirror); lane t keeps slot t % 8
+  if (HIST && hist) {
+    // chunk maxima: slot u's lane maxima, reduced over the group of eight
+    // lanes by a reduce-scatter of three exchanges (partner 7 - i, i ^ 2,
+    // i ^ 1), each lane keeping the half of its slots whose index bit
+    // matches its own lane bit and sending the other half: lane t ends with
+    // the maximum of slot t % 8
     const uint32_t ninf = __float_as_uint(-INFINITY);
-    uint32_t mine = 0;
+    const int li = t & (kChunkLanes - 1);
+    float c4[4], c2[2];
 #pragma unroll
-    for (int u = 0; u < kVecPerThread; ++u) {
-      float c = vec_elem(buf[u], 0, DT);
-#pragma unroll
-      for (int e = 1; e < EPV; ++e) c = fmaxf(c, vec_elem(buf[u], e, DT));
-      c = fmaxf(c, __uint_as_float(dpp_u32<kDppXor1>(ninf, __float_as_uint(c))));
-      c = fmaxf(c, __uint_as_float(dpp_u32<kDppXor2>(ninf, __float_as_uint(c))));
-      c = fmaxf(c, __uint_as_float(dpp_u32<kDppHalfMirror>(ninf, __float_as_uint(c))));
-      mine = (t & (kChunkLanes - 1)) == u ? f32_hi_up(c) : mine;
+    for (int j = 0; j < 4; ++j) {
+      const float keep = li & 4 ? mu[j + 4] : mu[j], send = li & 4 ? mu[j] : mu[j + 4];
+      c4[j] = fmaxf(keep, __uint_as_float(dpp_u32<kDppHalfMirror>(ninf, __float_as_uint(send))));
     }
-    cmax[t] = (uint16_t)mine;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float keep = li & 2 ? c4[j + 2] : c4[j], send = li & 2 ? c4[j] : c4[j + 2];
+      c2[j] = fmaxf(keep, __uint_as_float(dpp_u32<kDppXor2>(ninf, __float_as_uint(send))));
+    }
+    const float keep = li & 1 ? c2[1] : c2[0], send = li & 1 ? c2[0] : c2[1];
+    const float got = __uint_as_float(dpp_u32<kDppXor1>(ninf, __float_as_uint(send)));
+    cmax[t] = (uint16_t)f32_hi_up(fmaxf(keep, got));
     float M = sm[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, sm[w]);
