@@ -180,6 +180,38 @@ def test_topp_count_path_and_fallback(shift, T, top_p, counts):
     _check(w)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("top_p", [0.9, 0.97])
+def test_topp_nucleus_at_split_edges(dtype, top_p):
+    """A low background with a few large logits at the ends of the streaming
+    splits (the scalar head and tail elements of a misaligned row, the
+    first and last lines of a split, the row's last partial line): the top-p
+    gather reads only the lines whose recorded maximum can reach the band,
+    and the nucleus edge falls among these elements (top_p 0.9) or in the
+    background (0.97)."""
+    split = 8192 if dtype == "f32" else 16384
+    B, K, V = 3, 2, 3 * split + 5
+    rng = np.random.default_rng(split + int(1000 * top_p))
+    t32 = (rng.normal(0, 1, (B, K + 1, V)) - 8.0).astype(np.float32)
+    spots = [0, 1, 2, 3, split - 1, split, split + 1, 2 * split - 3, 2 * split + 2,
+             3 * split - 1, 3 * split, 3 * split + 1, V - 2, V - 1]
+    for b in range(B):
+        for i in range(K + 1):
+            t32[b, i, spots] = rng.uniform(2.0, 4.0, len(spots)).astype(np.float32)
+    d32 = (t32[:, :K] + rng.normal(0, 0.3, (B, K, V))).astype(np.float32)
+    tp = float(np.float32(top_p))
+    target, draft = W._to_dtype(t32, dtype), W._to_dtype(d32, dtype)
+    tf, df = W.logits_as_f32(target, dtype), W.logits_as_f32(draft, dtype)
+    assert all(_topp_uses_counts(tf[b, i], 1.0, tp, V) for b in range(B) for i in range(K + 1))
+    assert all(_topp_uses_counts(df[b, i], 1.0, tp, V) for b in range(B) for i in range(K))
+    toks = W.drafter_tokens(df, 1.0, tp, rng)
+    w = W.Workload("sample", f"top-p split edges {dtype} p={top_p}", B, K, V, dtype, target,
+                   draft, toks, W.uniforms_on_grid(rng, (B, K)), W.uniforms_on_grid(rng, (B,)),
+                   1.0, tp)
+    for off in (0, 1):
+        _check(w, offset=off)
+
+
 def test_flat_rows_and_neg_inf():
     rng = np.random.default_rng(4)
     B, K, V = 4, 3, 3000
