@@ -38,6 +38,7 @@ constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kBins = 256;
 constexpr float kBinsPerLog2 = 8.f;
 constexpr int kCand = 4096;  // keys of the selected bin or band held in LDS
+constexpr int kMergeSplits = 20;  // splits' counts staged in LDS at a time (30 KB)
 // Slack on the count bounds: covers the fp32 rounding of grid positions
 // (|M kk| < 2^18: under 0.03 of a bin, a factor 3.4e-4) and of the masses;
 // a wider slack only widens the band.
@@ -181,7 +182,6 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
       s_bhi = kHistBins;
     }
   }
-  for (int i = t; i < kHistBins; i += kTopThreads) cntf[i] = 0u;
   __syncthreads();
   const float M = sM;
   const double Z = sZ;
@@ -216,50 +216,69 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
   const double goal = top_p * Z;
   const float F = floorf(M * kk);
 
-  // merge the splits' counts: split s's bin j is the row's bin j + floor(M
-  // kk) - floor(m_s kk).  Work item i = (split, 16 bins): a batch of
-  // 16-byte loads is issued before any count is added.  A saturated count
-  // (some bin of a split holds more than kCountSat elements) leaves the row
-  // to the fallback.
+  // merge the splits' counts: split s's bin j is the row's bin j + off_s,
+  // off_s = floor(M kk) - floor(m_s kk) >= 0.  Up to kMergeSplits splits at
+  // a time are staged in LDS by 16-byte loads; thread t then sums row bins
+  // t + 512 r over the staged splits, reading stage[s][J - off_s] (lanes
+  // read consecutive bytes: no bank conflicts, no atomics).  A saturated
+  // count (some bin of a split holds more than kCountSat elements) leaves
+  // the row to the fallback.
+  __shared__ uint32_t stage[kMergeSplits][kHistBins / 4];
+  __shared__ int s_off[kMergeSplits];
   __shared__ int s_sat;
   if (t == 0) s_sat = 0;
-  __syncthreads();
-  {
-    const uint8_t *h0 = a.part_h + (size_t)row * S * kHistBins;
-    constexpr int kChunks = kHistBins / 16;  // 16-byte chunks per split
-    const int items = S * kChunks;
-    for (int i0 = t; i0 < items; i0 += 8 * kTopThreads) {
-      u32x4 v[8];
+  constexpr int kChunks = kHistBins / 16;  // 16-byte items per split
+  constexpr int kPer = kHistBins / kTopThreads;  // row bins per thread
+  constexpr int kStageIt = (kMergeSplits * kChunks + kTopThreads - 1) / kTopThreads;
+  const uint8_t *h0 = a.part_h + (size_t)row * S * kHistBins;
+  unsigned acc[kPer];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kTopThreads;
-        if (i < items) v[u] = reinterpret_cast<const u32x4 *>(h0)[i];
-      }
+  for (int r = 0; r < kPer; ++r) acc[r] = 0u;
+  bool sat = false;
+  for (int g0 = 0; g0 < S; g0 += kMergeSplits) {
+    const int gs = min(kMergeSplits, S - g0), items = gs * kChunks;
+    u32x4 v[kStageIt];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * kTopThreads;
-        if (i >= items) continue;
-        const int sp = i / kChunks, j0 = (i - sp * kChunks) * 16;
-        const float ms = payload_f32(pm[sp]);
-        if (!(ms > -INFINITY)) continue;
-        const int off = (int)(F - floorf(ms * kk));
+    for (int u = 0; u < kStageIt; ++u) {
+      const int i = t + u * kTopThreads;
+      if (i < items) v[u] = reinterpret_cast<const u32x4 *>(h0 + (size_t)g0 * kHistBins)[i];
+    }
+    if (t < gs) {
+      const float ms = payload_f32(pm[g0 + t]);
+      s_off[t] = ms > -INFINITY ? (int)(F - floorf(ms * kk)) : -1;  // -1: an empty split
+    }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const unsigned c = (v[u][e >> 2] >> (8 * (e & 3))) & 0xFFu;
-          const int jj = j0 + e + off;
-          if (c && jj < kHistBins) atomicAdd(&cntf[jj], c);
-          if (c == kCountSat) s_sat = 1;
-        }
+    for (int u = 0; u < kStageIt; ++u) {
+      const int i = t + u * kTopThreads;
+      if (i < items) {
+        reinterpret_cast<u32x4 *>(&stage[0][0])[i] = v[u];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)  // a byte 0xFF: a zero byte of ~w
+          sat |= ((~v[u][q] - 0x01010101u) & v[u][q] & 0x80808080u) != 0u;
       }
     }
+    __syncthreads();
+    for (int sp = 0; sp < gs; ++sp) {
+      const int off = s_off[sp];
+      if (off < 0) continue;
+      const uint8_t *hs = reinterpret_cast<const uint8_t *>(&stage[sp][0]);
+#pragma unroll
+      for (int r = 0; r < kPer; ++r) {
+        const int j = t + r * kTopThreads - off;
+        if (j >= 0) acc[r] += hs[j];
+      }
+    }
+    __syncthreads();
   }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) cntf[t + r * kTopThreads] = acc[r];
+  if (sat) s_sat = 1;
   __syncthreads();
   // running upper / lower bounds of the mass from the top: b_lo = the first
   // bin where the upper bound reaches the goal, b_hi = the first where the
   // lower bound does
   {
-    constexpr int kPer = kHistBins / kTopThreads;  // 3 bins per thread
-    const float phi = M * kk - F;                  // in [0, 1)
+    const float phi = M * kk - F;  // in [0, 1)
     double up[kPer], lo[kPer], su = 0.0, sl = 0.0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
