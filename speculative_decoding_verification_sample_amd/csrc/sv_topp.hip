@@ -622,12 +622,41 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
   const unsigned ncand = s_ncand;
   const bool in_lds = ncand <= (unsigned)kCand;
 
+  // keys held in LDS: the rounds start at the first byte where the smallest
+  // and largest key differ (a round above it would find one non-empty bin
+  // and add no mass above it)
+  int shift0 = 24;
+  if (in_lds && ncand > 0) {
+    __shared__ uint32_t s_klo, s_khi;
+    if (t == 0) {
+      s_klo = 0xFFFFFFFFu;
+      s_khi = 0u;
+    }
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (unsigned i = t; i < ncand; i += kTopThreads) {
+      lo = min(lo, cand[i]);
+      hi = max(hi, cand[i]);
+    }
+    hi = (uint32_t)wave_max_u64(hi);
+    lo = ~(uint32_t)wave_max_u64((uint64_t)~lo);
+    __syncthreads();
+    if (lane_id() == 0) {
+      atomicMin(&s_klo, lo);
+      atomicMax(&s_khi, hi);
+    }
+    __syncthreads();
+    const uint32_t d = s_klo ^ s_khi;
+    shift0 = d ? ((31 - __builtin_clz(d)) >> 3) << 3 : 0;
+    if (t == 0 && shift0 < 24) s_prefix = s_klo >> (shift0 + 8);
+    __syncthreads();
+  }
+
   // exact cut among the gathered keys (the band, or the selected bin):
   // radix rounds over value keys, accumulating mass from the top; if they
   // did not fit in LDS, each round reads the row again
   __shared__ double exc[kBins], rtot[kBins / 64];
   __shared__ int s_first, s_lastnz;
-  for (int shift = 24; shift >= 0 && !s_done; shift -= 8) {
+  for (int shift = shift0; shift >= 0 && !s_done; shift -= 8) {
     if (t < kBins) {
       mass[t] = 0.0;
       cnt[t] = 0;
