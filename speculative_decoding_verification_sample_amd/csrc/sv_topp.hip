@@ -331,8 +331,11 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
 constexpr int kGWin = kTopThreads / 16;             // splits per window (16 lanes a split's scalars)
 constexpr int kGWinEnt = kGWin * kChunksPerSplit;   // chunk entries per window
 constexpr int kGRounds = kGWinEnt / (8 * kTopThreads);  // 16-byte loads of entries per lane
-constexpr int kGSlots = 8;                          // chunk lines per lane group and pass
-constexpr int kGPerPass = kTopThreads / kChunkLanes * kGSlots;
+// chunk lines per lane group and pass: 8 for fp32; 2 for bf16 (eight slots
+// of eight bf16 elements took 214 registers, one workgroup per CU; two take
+// 95, and the bf16 top-p call ran 577 -> 564 us at B256 K4 V152064)
+template <int DT>
+constexpr int gather_slots() { return DT == kBF16 ? 2 : 8; }
 
 // Exclusive prefix of v over the workgroup; *total gets the sum.  Whole
 // workgroup; wtot is free again on return.
@@ -441,6 +444,8 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_gather(SampleArgs a) {
     // passes over the listed lines: lane group t / 8 takes items t / 8 +
     // 64 r, lane t one 16-byte vector of each (entry g * 8 + u of a split
     // is its vectors 8 g .. 8 g + 7 of slot u: v = 8 g + lane + u kThreads)
+    constexpr int kGSlots = gather_slots<DT>();
+    constexpr int kGPerPass = kTopThreads / kChunkLanes * kGSlots;
     for (int p0 = 0; p0 == 0 || p0 < n; p0 += kGPerPass) {
       // every list read first, then every load
       int ent[kGSlots];
