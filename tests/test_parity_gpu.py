@@ -212,6 +212,27 @@ def test_topp_nucleus_at_split_edges(dtype, top_p):
         _check(w, offset=off)
 
 
+def test_topp_many_splits():
+    """More than 32 streaming splits per row (the gather works in windows of
+    32 splits, the band merges the counts of 20 splits at a time), the
+    nucleus spread over the first and the last window."""
+    B, K, V = 2, 1, 8192 * 33 + 7
+    rng = np.random.default_rng(33)
+    t32 = (rng.normal(0, 1, (B, K + 1, V)) - 11.0).astype(np.float32)
+    spots = np.concatenate([rng.integers(0, 8192 * 2, 6), rng.integers(8192 * 32, V, 6)])
+    for b in range(B):
+        for i in range(K + 1):
+            t32[b, i, spots] = rng.uniform(2.0, 4.0, len(spots)).astype(np.float32)
+    d32 = (t32[:, :K] + rng.normal(0, 0.3, (B, K, V))).astype(np.float32)
+    for top_p in (0.9, 0.99):
+        tp = float(np.float32(top_p))
+        assert all(_topp_uses_counts(t32[b, i], 1.0, tp, V) for b in range(B) for i in range(K + 1))
+        toks = W.drafter_tokens(d32, 1.0, tp, rng)
+        w = W.Workload("sample", f"top-p 34 splits p={top_p}", B, K, V, "f32", t32, d32, toks,
+                       W.uniforms_on_grid(rng, (B, K)), W.uniforms_on_grid(rng, (B,)), 1.0, tp)
+        _check(w, offset=1)
+
+
 def test_flat_rows_and_neg_inf():
     rng = np.random.default_rng(4)
     B, K, V = 4, 3, 3000
