@@ -42,7 +42,8 @@ def lib():
         P = ctypes.c_void_p
         I = ctypes.c_int
         D = ctypes.c_double
-        L.oracle_verify_sample.argtypes = [P, P, I, P, P, P, D, D, I, I, I, P, P, P, P, P, P, P]
+        L.oracle_verify_sample.argtypes = [P, P, I, P, P, P, D, D, I, I, I, P, P, P, P, P, P, P,
+                                           P, P, P, P, P]
         L.oracle_verify_sample.restype = I
         L.oracle_verify_greedy.argtypes = [P, I, P, I, I, I, P, P, P]
         L.oracle_verify_greedy.restype = I
@@ -93,6 +94,12 @@ def row_distribution(logits: np.ndarray, temperature: float, top_p: float = 1.0)
 
 def verify_sample(target, draft, tokens, u_accept, u_sample, temperature, top_p=1.0,
                   row_info=False):
+    """Sampling verify (oracle.c, oracle_verify_sample).  Besides the
+    outputs it returns, per request, the variants with one row's nucleus cut
+    moved by one tie group where that row's cumulative mass before or after
+    its cut group lies within 1e-6 of top_p: `alt_n`, `alt_token`, `alt_S`
+    [B, 2K+1, 2] (alt_n -1: no variant) and `alt_p`, `alt_q` [B, 2K+1, 2, K];
+    alternative [row, 0] moves the cut one group earlier, [row, 1] later."""
     target = np.ascontiguousarray(target)
     draft = np.ascontiguousarray(draft)
     if draft.dtype != target.dtype:
@@ -106,12 +113,19 @@ def verify_sample(target, draft, tokens, u_accept, u_sample, temperature, top_p=
     assert tokens.shape == (B, K) and ua.shape == (B, K) and us.shape == (B,)
     out = dict(accepted=np.empty(B, np.int32), tokens=np.empty((B, K + 1), np.int32),
                p=np.empty((B, K), np.float64), q=np.empty((B, K), np.float64),
-               S=np.empty(B, np.float64), flags=np.empty(B, np.int32))
+               S=np.empty(B, np.float64), flags=np.empty(B, np.int32),
+               alt_n=np.empty((B, 2 * K + 1, 2), np.int32),
+               alt_token=np.empty((B, 2 * K + 1, 2), np.int32),
+               alt_S=np.empty((B, 2 * K + 1, 2), np.float64),
+               alt_p=np.zeros((B, 2 * K + 1, 2, K), np.float64),
+               alt_q=np.zeros((B, 2 * K + 1, 2, K), np.float64))
     info = np.empty((B, 2 * K + 1, 7), np.float64) if row_info else None
     rc = lib().oracle_verify_sample(
         _p(target), _p(draft), _dtype_code(target), _p(tokens), _p(ua), _p(us),
         float(temperature), float(top_p), B, K, V, _p(out["accepted"]), _p(out["tokens"]),
-        _p(out["p"]), _p(out["q"]), _p(out["S"]), _p(out["flags"]), _p(info))
+        _p(out["p"]), _p(out["q"]), _p(out["S"]), _p(out["flags"]), _p(info),
+        _p(out["alt_n"]), _p(out["alt_token"]), _p(out["alt_S"]), _p(out["alt_p"]),
+        _p(out["alt_q"]))
     if rc != 0:
         raise ValueError(f"oracle_verify_sample: {rc}")
     if row_info:
@@ -213,7 +227,11 @@ def verify_mixed(target, draft, tokens, u_accept, u_sample, temperature, top_p=N
     top_p = np.ones(B, np.float32) if top_p is None else np.asarray(top_p, np.float32)
     out = dict(accepted=np.empty(B, np.int32), tokens=np.empty((B, K + 1), np.int32),
                p=np.zeros((B, K)), q=np.zeros((B, K)), S=np.zeros(B),
-               flags=np.zeros(B, np.int32))
+               flags=np.zeros(B, np.int32),
+               alt_n=np.full((B, 2 * K + 1, 2), -1, np.int32),
+               alt_token=np.full((B, 2 * K + 1, 2), -1, np.int32),
+               alt_S=np.zeros((B, 2 * K + 1, 2)), alt_p=np.zeros((B, 2 * K + 1, 2, K)),
+               alt_q=np.zeros((B, 2 * K + 1, 2, K)))
     for b in range(B):
         T, P = float(temperature[b]), float(top_p[b])
         if not (np.isfinite(T) and T >= 0.0) or not (0.0 < P <= 1.0):
@@ -225,7 +243,8 @@ def verify_mixed(target, draft, tokens, u_accept, u_sample, temperature, top_p=N
         else:
             r = verify_sample(target[b:b + 1], draft[b:b + 1], tokens[b:b + 1],
                               u_accept[b:b + 1], u_sample[b:b + 1], T, P)
-            for key in ("p", "q", "S", "flags"):
+            for key in ("p", "q", "S", "flags", "alt_n", "alt_token", "alt_S", "alt_p",
+                        "alt_q"):
                 out[key][b] = r[key][0]
         out["accepted"][b] = r["accepted"][0]
         out["tokens"][b] = r["tokens"][0]

@@ -285,13 +285,27 @@ static SampleResult verify_one_request(
  * replacement or bonus, then -1); optional out_p/out_q [B, K] (p'(x_i),
  * q'(x_i)), out_S [B] (residual mass), out_flags [B] (FLAG_* bits),
  * out_row_info [B, 2K+1, 7] (see row_distribution).
+ *
+ * The other nucleus membership (top_p < 1).  Where a row's cumulative mass
+ * before or after its cut group lies within 1e-6 of top_p, the request is
+ * verified again with that one row's cut moved one group earlier (before
+ * near) or later (after near), every other row as defined.  Each such
+ * variant is alternative a = 2 * row + (0: earlier, 1: later), row in
+ * [0, 2K] (target rows 0..K, draft rows K+1..2K).  Optional outputs, all
+ * indexed [B, 2K+1, 2]: out_alt_n (the accepted length under the variant,
+ * -1 where no variant is taken), out_alt_token (its replacement or bonus),
+ * out_alt_S (its residual mass); out_alt_p / out_alt_q [B, 2K+1, 2, K] its
+ * p'(x_i), q'(x_i).  FLAG_TOPP_NEAR marks a request where some variant's
+ * accepted length or token differs from the defined one.
  */
 int oracle_verify_sample(const void *target, const void *draft, int dtype,
                          const int32_t *tokens, const float *u_accept,
                          const float *u_sample, double T, double top_p, int B,
                          int K, int V, int32_t *out_accepted, int32_t *out_tokens,
                          double *out_p, double *out_q, double *out_S,
-                         int32_t *out_flags, double *out_row_info) {
+                         int32_t *out_flags, double *out_row_info,
+                         int32_t *out_alt_n, int32_t *out_alt_token, double *out_alt_S,
+                         double *out_alt_p, double *out_alt_q) {
   if (!target || !draft || !tokens || !u_accept || !u_sample || !out_accepted ||
       !out_tokens)
     return -1;
@@ -320,7 +334,16 @@ int oracle_verify_sample(const void *target, const void *draft, int dtype,
         infos);
     /* a nucleus whose edge sits within 1e-6 of top_p: does the other choice
      * change what is emitted? */
+    const size_t nalt = (size_t)(2 * K + 1) * 2;
+    if (out_alt_n)
+      for (size_t a = 0; a < nalt; ++a) {
+        out_alt_n[(size_t)b * nalt + a] = -1;
+        if (out_alt_token) out_alt_token[(size_t)b * nalt + a] = -1;
+        if (out_alt_S) out_alt_S[(size_t)b * nalt + a] = 0.0;
+      }
     if (top_p < 1.0) {
+      /* infos[] of the defined request, kept: the variants below overwrite
+       * nothing of it (they pass no info buffer) */
       for (int row = 0; row < 2 * K + 1; ++row) {
         double before = infos[row][4], after = infos[row][5];
         int shifts[2] = {0, 0};
@@ -329,10 +352,15 @@ int oracle_verify_sample(const void *target, const void *draft, int dtype,
         if (shifts[0] || shifts[1]) res.flags |= FLAG_TOPP_EDGE;
         for (int s = 0; s < 2; ++s) {
           if (!shifts[s]) continue;
-          SampleResult alt = verify_one_request(tb, db, dtype, tok, ua, u_sample[b], T,
-                                                top_p, K, V, row, shifts[s], P, Q,
-                                                scratch, r, NULL, NULL, NULL);
+          const size_t a = (size_t)b * nalt + (size_t)(2 * row + s);
+          SampleResult alt = verify_one_request(
+              tb, db, dtype, tok, ua, u_sample[b], T, top_p, K, V, row, shifts[s], P, Q,
+              scratch, r, out_alt_p ? out_alt_p + a * (size_t)K : NULL,
+              out_alt_q ? out_alt_q + a * (size_t)K : NULL, NULL);
           if (alt.n != res.n || alt.token != res.token) res.flags |= FLAG_TOPP_NEAR;
+          if (out_alt_n) out_alt_n[a] = alt.n;
+          if (out_alt_token) out_alt_token[a] = alt.token;
+          if (out_alt_S) out_alt_S[a] = alt.S;
         }
       }
       if (out_row_info)

@@ -60,11 +60,20 @@ def test_random_trees_match_the_generator_layout_and_are_valid():
     c2 = rng.random((B, n + 1)).astype(np.float32)
     o = oracle.tree_merge(p1, t1, c1, p2, t2, c2)
     for b in range(B):
-        par, tok, mask = W.merge_two_trees(p1[b], t1[b], W.ancestor_mask(p1[b]),
-                                           p2[b], t2[b], W.ancestor_mask(p2[b]))
+        par, tok, mask = W.merge_two_trees(p1[b], t1[b], p2[b], t2[b])
         np.testing.assert_array_equal(o["parents"][b], par)
         np.testing.assert_array_equal(o["tokens"][b], tok)
         np.testing.assert_array_equal(o["mask"][b], mask)
+        # the block structure, as properties: the root sees only itself;
+        # each tree's rows keep that tree's own ancestor sets (the root
+        # standing for both roots) and see nothing of the other tree
+        m = o["mask"][b]
+        m1, m2 = W.ancestor_mask(p1[b]), W.ancestor_mask(p2[b])
+        assert m[0].tolist() == [1] + [0] * (2 * n)
+        np.testing.assert_array_equal(m[1:n + 1, :n + 1], m1[1:])
+        assert not m[1:n + 1, n + 1:].any() and not m[n + 1:, 1:n + 1].any()
+        np.testing.assert_array_equal(m[n + 1:, 0], m2[1:, 0])
+        np.testing.assert_array_equal(m[n + 1:, n + 1:], m2[1:, 1:])
         assert oracle.tree_is_valid(o["parents"][b], o["mask"][b])
         m1, m2 = c1[b, 1:].astype(np.float64).mean(), c2[b, 1:].astype(np.float64).mean()
         assert abs(o["conf"][b, 0] - m1) < 1e-15 and abs(o["conf"][b, 1] - m2) < 1e-15

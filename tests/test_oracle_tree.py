@@ -83,8 +83,7 @@ def test_merged_mask_layout_golden():
     g = json.load(open(os.path.join(GOLDEN, "merged_mask_layout.json")))
     p1 = np.array(g["tree1_parents"], np.int32)
     p2 = np.array(g["tree2_parents"], np.int32)
-    par, tok, mask = W.merge_two_trees(p1, np.arange(len(p1)), W.ancestor_mask(p1),
-                                       p2, 100 + np.arange(len(p2)), W.ancestor_mask(p2))
+    par, tok, mask = W.merge_two_trees(p1, np.arange(len(p1)), p2, 100 + np.arange(len(p2)))
     np.testing.assert_array_equal(mask, np.array(g["merged_mask"], np.uint8))
     np.testing.assert_array_equal(par, np.array(g["merged_parents"], np.int32))
     assert list(tok) == [0, 1, 2, 3, 101, 102]

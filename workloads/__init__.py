@@ -157,29 +157,22 @@ def ancestor_mask(parents: np.ndarray) -> np.ndarray:
     return m
 
 
-def merge_two_trees(parents1, tokens1, mask1, parents2, tokens2, mask2):
-    """Merge two drafters' trees under tree 1's root, following the block
-    layout of the TAPS page (aitrends.kr, "코드 예제" tree-merge routine):
-    node 0 is the shared root (its mask row is itself only); tree 1's
-    non-root nodes keep their indices 1..n1 and their mask rows, root column
-    included; tree 2's non-root nodes follow at n1+1.., their rows get the
-    root column plus tree 2's own non-root block shifted by n1.  Tokens are
-    tree 1's (root included) followed by tree 2's non-root tokens."""
-    n1 = len(parents1) - 1
-    n2 = len(parents2) - 1
-    N = n1 + n2 + 1
-    mask = np.zeros((N, N), dtype=np.uint8)
-    mask[0, 0] = 1
-    mask[1:n1 + 1, :n1 + 1] = mask1[1:, :]
-    mask[n1 + 1:, 0] = 1
-    mask[n1 + 1:, n1 + 1:] = mask2[1:, 1:]
-    parents = np.empty(N, dtype=np.int32)
-    parents[:n1 + 1] = parents1
-    p2 = np.asarray(parents2[1:], dtype=np.int64)
-    parents[n1 + 1:] = np.where(p2 == 0, 0, p2 + n1).astype(np.int32)
-    tokens = np.concatenate([np.asarray(tokens1, np.int32),
-                             np.asarray(tokens2[1:], np.int32)])
-    return parents, tokens, mask
+def merge_two_trees(parents1, tokens1, parents2, tokens2):
+    """Two drafters' trees under one shared root (TAPS, aitrends.kr, section
+    "방법론": both trees verified in one target pass under a mask that keeps
+    each branch blind to the other).  Node numbering: the shared root first
+    (it carries tree 1's root token), then tree 1's non-root nodes in their
+    own order, then tree 2's; a tree-2 node hanging from its root hangs from
+    the shared root, any other tree-2 parent index moves up by n1 (tree 1's
+    non-root node count).  The mask is the ancestor-or-self closure of the
+    merged parents.  Returns (parents[N], tokens[N], mask[N, N]), N = n1 + n2 + 1."""
+    p1 = np.asarray(parents1, np.int64)
+    p2 = np.asarray(parents2, np.int64)
+    n1 = len(p1) - 1
+    moved = np.where(p2[1:] == 0, 0, p2[1:] + n1)
+    parents = np.concatenate([p1, moved]).astype(np.int32)
+    tokens = np.concatenate([np.asarray(tokens1, np.int32), np.asarray(tokens2, np.int32)[1:]])
+    return parents, tokens, ancestor_mask(parents)
 
 
 # --------------------------------------------------------------------------
@@ -299,10 +292,9 @@ def tree_merged(cfg: int, B: int, n_per_tree: int, V: int, dtype: str = "bf16",
     for b in range(B):
         p1 = grow_tree(r["tree"], n_per_tree, max_depth, max_children)
         p2 = grow_tree(r["tree"], n_per_tree, max_depth, max_children)
-        m1, m2 = ancestor_mask(p1), ancestor_mask(p2)
         zeros1 = np.zeros(len(p1), np.int32)
         zeros2 = np.zeros(len(p2), np.int32)
-        par, _, mask = merge_two_trees(p1, zeros1, m1, p2, zeros2, m2)
+        par, _, mask = merge_two_trees(p1, zeros1, p2, zeros2)
         tok = np.empty(N, np.int32)
         tok[0] = int(r["tokens"].integers(0, V))
         for i in range(1, N):
@@ -388,7 +380,7 @@ def random_paths(rng: np.random.Generator, B: int, n_per_tree: int):
         p1 = grow_tree(rng, n_per_tree)
         p2 = grow_tree(rng, n_per_tree)
         zeros = np.zeros(n_per_tree + 1, np.int32)
-        par, _, _ = merge_two_trees(p1, zeros, ancestor_mask(p1), p2, zeros, ancestor_mask(p2))
+        par, _, _ = merge_two_trees(p1, zeros, p2, zeros)
         node = int(rng.integers(N))
         chain = []
         while node > 0:
