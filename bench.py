@@ -268,7 +268,11 @@ def main():
     achieved = algo_bytes / (kern_us * 1e-6) / 1e9
     step_gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
     cpu = cpu_baseline(w0, args.cpu_seconds) if args.cpu_seconds > 0 else None
-    cpu_pool = cpu_baseline_threads(w0, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    outcomes = {}
+    cpu_pool = (cpu_baseline_threads(w0, args.cpu_seconds, outcomes)
+                if args.cpu_seconds > 0 else None)
+    agreement = (oracle_agreement(w0, first, outcomes)
+                 if args.cpu_seconds > 0 and args.workload != "mixed" else None)
     traffic = counters_for(args.workload, kernel)
     result = {
         "metric": METRIC,
@@ -302,7 +306,14 @@ def main():
         "call_us": call_us,
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_pool,
+        "oracle_agreement": agreement,
     }
+    if not single_launch:
+        # several launches per call: the whole call against the same bytes
+        call_gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
+        result["roofline"]["whole_call"] = {
+            "achieved": call_gbs, "frac": call_gbs / HBM_PEAK_GBS, "us": ms_per_step * 1000.0,
+            "note": "algorithmic bytes over the timed region's per-step time (all launches)"}
     print(json.dumps(result), flush=True)
 
 
@@ -553,6 +564,18 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n * 4, "launches": 20}), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, seconds):
     """The CPU oracle, single-threaded and pinned to one core, on consecutive
     requests of the same workload (whole-call arithmetic per request), for
@@ -589,14 +612,15 @@ def _cpu_single(w, seconds):
             "kind": "oracle",
             "requests_per_s": done / el,
             "sample": f"{done} requests of {w.name} in oracle calls of {n} request(s), "
-                      f"{el:.1f}s single-threaded on one core of {platform.processor() or platform.machine()} "
+                      f"{el:.1f}s single-threaded on one core of {cpu_model()} "
                       f"({os.cpu_count()} cpus visible)"}
 
 
-def cpu_baseline_threads(w, seconds):
+def cpu_baseline_threads(w, seconds, outcomes=None):
     """The same oracle fanned out over requests on every core this process
     may use (one thread per core; the oracle's C code runs outside the
-    interpreter lock), for about `seconds`."""
+    interpreter lock), for about `seconds`.  `outcomes` (a dict) receives
+    the oracle's result for each request index it verified."""
     import concurrent.futures as cf
     import oracle
     import workloads as W
@@ -608,7 +632,9 @@ def cpu_baseline_threads(w, seconds):
     def worker(k):
         i = k
         while time.perf_counter() - t0 < seconds:
-            oracle.verify_workload(W.subset(w, [i % w.B]))
+            r = oracle.verify_workload(W.subset(w, [i % w.B]))
+            if outcomes is not None and (i % w.B) not in outcomes:
+                outcomes[i % w.B] = r
             done[k] += 1
             i += n_thr
 
@@ -620,7 +646,39 @@ def cpu_baseline_threads(w, seconds):
     return {"value": total * per_req / el, "unit": "positions/s", "cores": n_thr,
             "kind": "oracle", "requests_per_s": total / el,
             "sample": f"{total} requests of {w.name}, one request per oracle call, "
-                      f"{el:.1f}s on {n_thr} threads"}
+                      f"{el:.1f}s on {n_thr} threads of {cpu_model()}"}
+
+
+def oracle_agreement(w, first, outcomes):
+    """The first timed call's outputs against the oracle's, on the requests
+    the CPU baseline verified: per-flag request counts (a uniform within 1e-6
+    relative of its threshold or CDF step; a nucleus edge within 1e-6 of
+    top_p) and the requests, outside the flagged ones, whose accepted length
+    or tokens differ."""
+    import numpy as np
+    import oracle
+    if not outcomes:
+        return None
+    idx = sorted(outcomes)
+    key = "accepted" if w.kind != "tree" else "path_len"
+    acc = first[key].cpu().numpy()
+    tok = first["tokens"].cpu().numpy()
+    flags = np.array([int(outcomes[i]["flags"][0]) if "flags" in outcomes[i] else 0 for i in idx])
+    amb = (flags & (oracle.FLAG_ACCEPT_NEAR | oracle.FLAG_CDF_NEAR | oracle.FLAG_S_NEAR)) != 0
+    near = (flags & oracle.FLAG_TOPP_NEAR) != 0
+    mism = 0
+    for j, i in enumerate(idx):
+        same = acc[i] == outcomes[i][key][0] and (tok[i] == outcomes[i]["tokens"][0]).all()
+        if not same and not amb[j] and not near[j]:
+            mism += 1
+    return {"requests_compared": len(idx), "unflagged_mismatches": mism,
+            "flagged": {"accept_near": int(((flags & oracle.FLAG_ACCEPT_NEAR) != 0).sum()),
+                        "cdf_near": int(((flags & oracle.FLAG_CDF_NEAR) != 0).sum()),
+                        "s_near": int(((flags & oracle.FLAG_S_NEAR) != 0).sum()),
+                        "topp_near": int(near.sum()),
+                        "topp_edge": int(((flags & oracle.FLAG_TOPP_EDGE) != 0).sum())},
+            "note": "oracle outcomes from the CPU baseline's own runs; topp_near requests "
+                    "may take either nucleus membership"}
 
 
 if __name__ == "__main__":

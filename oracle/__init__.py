@@ -17,8 +17,9 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
 FLAG_ACCEPT_NEAR, FLAG_CDF_NEAR, FLAG_TOPP_NEAR, FLAG_FALLBACK, FLAG_TOKEN_RANGE = 1, 2, 4, 8, 16
-FLAG_TOPP_EDGE = 32
-FLAG_AMBIGUOUS = FLAG_ACCEPT_NEAR | FLAG_CDF_NEAR | FLAG_TOPP_NEAR
+FLAG_TOPP_EDGE, FLAG_S_NEAR = 32, 64
+FLAG_AMBIGUOUS = FLAG_ACCEPT_NEAR | FLAG_CDF_NEAR | FLAG_TOPP_NEAR | FLAG_S_NEAR
+S_RESOLUTION = 2.0 ** -20  # residual mass taken as empty (draw from p')
 
 _lib = None
 

@@ -47,12 +47,19 @@
 #define FLAG_ACCEPT_NEAR 1   /* a uniform within 1e-6 relative of p'/q' */
 #define FLAG_CDF_NEAR 2      /* u*S within 1e-6 relative of a CDF step */
 #define FLAG_TOPP_NEAR 4     /* an alternative nucleus near top_p changes the output */
-#define FLAG_FALLBACK 8      /* residual mass S <= 0, drew from p' instead */
+#define FLAG_FALLBACK 8      /* residual mass S <= S_RESOLUTION, drew from p' instead */
 #define FLAG_TOKEN_RANGE 16  /* a draft token outside [0, V) */
 #define FLAG_TOPP_EDGE 32    /* some row's nucleus edge lies within 1e-6 of top_p
                                 (informational: p', q' may legitimately differ) */
+#define FLAG_S_NEAR 64       /* residual mass within a factor 4 of S_RESOLUTION */
 
 #define REL_TOL 1e-6
+/* Residual mass at or below which the residual is taken as empty and the
+ * replacement is drawn from p' (reading: S = 0 cannot happen after a
+ * rejection in exact arithmetic; at 2^-20 of the unit mass, twice the total
+ * rounding of p' and q' held as float32 values, max(0, p' - q') carries no
+ * resolvable mass, and normalising it would only amplify rounding). */
+#define S_RESOLUTION 9.5367431640625e-07
 
 /* ------------------------------------------------------------------ */
 /* input widening: every stored value becomes the fp64 number it encodes */
@@ -236,7 +243,8 @@ static SampleResult verify_one_request(
       r[j] = d > 0.0 ? d : 0.0;
       S += r[j];
     }
-    if (!(S > 0.0)) {
+    if (S > 0.25 * S_RESOLUTION && S < 4.0 * S_RESOLUTION) res.flags |= FLAG_S_NEAR;
+    if (!(S > S_RESOLUTION)) {
       res.flags |= FLAG_FALLBACK;
       S = 0.0;
       for (int j = 0; j < V; ++j) {

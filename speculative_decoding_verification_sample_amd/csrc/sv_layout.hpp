@@ -73,13 +73,26 @@ struct Decision {
   int mode;             // kModeResidual or kModeBonus
   float m_t, m_d;       // maxima of target row n / draft row n
   float tau_t, tau_d;   // smallest kept logits (-inf: all kept)
-  float inv_t, inv_d;   // 1 / kept mass (the mass is at least 1); inv_d = 0 for the bonus draw (r = p')
+  // 1 / kept mass (the mass is at least 1) as an unevaluated fp32 pair hi + lo:
+  // one rounding of each inverse to fp32 would scale every p' (and every q')
+  // by its own factor within 2^-24 of 1, a shift that max(0, p' - q') does
+  // not cancel and that S magnifies when it is small; inv_d = 0 for the
+  // bonus draw (r = p')
+  float inv_t, inv_t_lo, inv_d, inv_d_lo;
 };
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
 
 // Largest number of residual splits per row (the draw stages them in LDS).
 constexpr int kMaxSplitsB = 512;
+
+// A residual mass S = sum max(0, p' - q') at or below 2^-20 of the unit mass
+// is taken as empty and the replacement is drawn from p' instead: S = 0 is
+// impossible after a rejection in exact arithmetic, and at this level (twice
+// the total rounding of p' and q' as float32 values, e.g. two equal rows
+// whose normalisers were summed in different orders) the residual holds
+// rounding alone.
+constexpr double kResidualResolution = 9.5367431640625e-07;
 
 // Top-p: a streaming tile also counts its split's elements by distance from
 // the split maximum on the grid floor(l * k * kHistPerLog2) (1/64 log2 unit,

@@ -77,18 +77,21 @@ __device__ __forceinline__ double prob_at(float l, float m, float tau, double zk
 }
 
 // Mass of one token of the drawn row pair: the residual r = max(0, p' - q')
-// (the bonus draw has w_d = 0, so r = p'), or p' itself (P: the fallback when
-// the residual mass is not positive).  Every pass over the pair computes it
-// with this one function, so the values agree bit for bit.  fp32: the terms
-// 2^((l - m) k) are fp32 values, so a wider product and difference would not
-// make r more accurate than their own rounding (each r within ~2e-7 of p';
-// the sums over a split run in fp64).
+// (the bonus draw has inv_d = 0, so r = p'), or p' itself (P: the fallback
+// when the residual mass is not positive).  Every pass over the pair computes
+// it with this one function, so the values agree bit for bit.  fp32 terms
+// 2^((l - m) k) times the inverse kept mass as a float pair (one fused
+// multiply-add: the product carries one rounding, and no common factor
+// separates p' from q'); the difference in fp32, the sums over a split in
+// fp64.
 template <bool TOPP, bool P>
 __device__ __forceinline__ double token_mass(float lt, float ld, const Decision &d, Scale k) {
-  float pt = tempered(lt, d.m_t, k) * d.inv_t;
+  const float et = tempered(lt, d.m_t, k);
+  float pt = fmaf(et, d.inv_t, et * d.inv_t_lo);
   if (TOPP) pt = lt >= d.tau_t ? pt : 0.f;
   if (P) return (double)pt;
-  float qd = tempered(ld, d.m_d, k) * d.inv_d;
+  const float ed = tempered(ld, d.m_d, k);
+  float qd = fmaf(ed, d.inv_d, ed * d.inv_d_lo);
   if (TOPP) qd = ld >= d.tau_d ? qd : 0.f;
   return (double)fmaxf(pt - qd, 0.f);
 }
@@ -295,15 +298,16 @@ __device__ __forceinline__ bool decide(const int32_t *tokens, const float *u_acc
       d.mode = n < K ? kModeResidual : kModeBonus;
       d.m_t = L.row_m[n];
       d.tau_t = L.row_tau[n];
-      d.inv_t = (float)(1.0 / L.row_zk[n]);
+      split_f64(1.0 / L.row_zk[n], &d.inv_t, &d.inv_t_lo);
       if (n < K) {
         d.m_d = L.row_m[K + 1 + n];
         d.tau_d = L.row_tau[K + 1 + n];
-        d.inv_d = (float)(1.0 / L.row_zk[K + 1 + n]);
+        split_f64(1.0 / L.row_zk[K + 1 + n], &d.inv_d, &d.inv_d_lo);
       } else {  // bonus: no draft row; its weight 0 makes the residual p'
         d.m_d = d.m_t;
         d.tau_d = d.tau_t;
         d.inv_d = 0.f;
+        d.inv_d_lo = 0.f;
       }
       *sd = d;
     }
@@ -685,7 +689,7 @@ __device__ __forceinline__ void residual_tile(const char *target, const char *dr
       double rem, total;
       const int split = pick_split_wave(t < SB ? D.tot[t] : 0.0, SB, us, &rem, &total);
       if (t == 0) {
-        s_use_p = !(total > 0.0);
+        s_use_p = !(total > kResidualResolution);
         s_split = split;
         s_rem = rem;
         s_total = total;
@@ -694,15 +698,16 @@ __device__ __forceinline__ void residual_tile(const char *target, const char *dr
   } else if (t == 0) {
     double rem, total;
     const int split = pick_split(D.tot, SB, us, &rem, &total);
-    s_use_p = !(total > 0.0);
+    s_use_p = !(total > kResidualResolution);
     s_split = split;
     s_rem = rem;
     s_total = total;
   }
-  // S <= 0 cannot happen in exact arithmetic after a rejection (the residual
+  // S = 0 cannot happen in exact arithmetic after a rejection (the residual
   // holds at least q'(x) - p'(x) > 0); it can when p' and q' agree and the
-  // draft token has no mass under either.  Then the last tile draws from p'
-  // instead (recomputed split by split: rare and slow).
+  // draft token has no mass under either.  An S at or below the resolution
+  // level (rounding alone) sends the last tile to draw from p' instead
+  // (recomputed split by split: rare and slow).
   __syncthreads();
   if (!s_use_p) {
     const int claim = s_split >= 0 ? s_split : SB - 1;

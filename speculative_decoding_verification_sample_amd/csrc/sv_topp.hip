@@ -613,14 +613,21 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
     }
     __syncthreads();
     // fallback 2. the selected bin's elements, gathered into LDS as value
-    //    keys (one more pass over the row)
+    //    keys: each thread counts its elements of the bin, then writes them
+    //    at offsets from a workgroup scan (two more passes over the row; the
+    //    keys land in the same order on every run)
     sel = s_bin;
     if (!s_done) {
+      __shared__ int wtot[kTopWaves];
+      int mine = 0, total = 0;
+      for_row<DT>(rp, V, [&](int, float x) { mine += dist_bin(x, M, kr) == sel; });
+      int slot = block_excl_scan(mine, wtot, &total);
       for_row<DT>(rp, V, [&](int, float x) {
         if (dist_bin(x, M, kr) != sel) return;
-        const unsigned slot = atomicAdd(&s_ncand, 1u);
-        if (slot < (unsigned)kCand) cand[slot] = key_of_f32(x);
+        if (slot < kCand) cand[slot] = key_of_f32(x);
+        ++slot;
       });
+      if (t == 0) s_ncand = (unsigned)total;
       __syncthreads();
     }
   }
@@ -658,12 +665,15 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
 
   // exact cut among the gathered keys (the band, or the selected bin):
   // radix rounds over value keys, accumulating mass from the top; if they
-  // did not fit in LDS, each round reads the row again
+  // did not fit in LDS, each round reads the row again.  Each wave adds its
+  // keys' masses into its own row of bins (a wave's adds come in program
+  // order), and the rows are summed in wave order, so the kept mass is the
+  // same bit for bit on every run; the counts and key bounds are integers.
   __shared__ double exc[kBins], rtot[kBins / 64];
   __shared__ int s_first, s_lastnz;
   for (int shift = shift0; shift >= 0 && !s_done; shift -= 8) {
+    for (int i = t; i < kTopWaves * kBins; i += kTopThreads) (&hist[0][0])[i] = 0.0;
     if (t < kBins) {
-      mass[t] = 0.0;
       cnt[t] = 0;
       kmin[t] = 0xFFFFFFFFu;
       kmax[t] = 0u;
@@ -677,7 +687,7 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
     auto visit = [&](uint32_t key) {
       if (shift < 24 && (key >> (shift + 8)) != prefix) return;
       const int sb = (key >> shift) & 0xFF;
-      atomicAdd(&mass[sb], (double)tempered(f32_of_key(key), M, k));
+      atomicAdd(&hist[w][sb], (double)tempered(f32_of_key(key), M, k));
       atomicAdd(&cnt[sb], 1u);
       atomicMin(&kmin[sb], key);
       atomicMax(&kmax[sb], key);
@@ -693,6 +703,13 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
           visit(key_of_f32(x));
         }
       });
+    }
+    __syncthreads();
+    if (t < kBins) {
+      double sum = 0.0;
+#pragma unroll
+      for (int u = 0; u < kTopWaves; ++u) sum += hist[u][t];
+      mass[t] = sum;
     }
     __syncthreads();
     // from the top bin down (lane t: bin 255 - t), the mass of the

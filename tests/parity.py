@@ -66,15 +66,21 @@ def variants(ref, r):
     return out
 
 
+# a uniform within 1e-6 relative of its accept threshold or CDF step, or a
+# residual mass near the level below which the draw falls back to p'
+EXCLUDED = oracle.FLAG_ACCEPT_NEAR | oracle.FLAG_CDF_NEAR | oracle.FLAG_S_NEAR
+
+
 def flag_counts(flags):
     """Requests per oracle flag, and the requests left out of the exact
-    comparison (a uniform within 1e-6 relative of its threshold or CDF step)."""
+    comparison (EXCLUDED)."""
     f = np.asarray(flags)
     return {"accept_near": int(((f & oracle.FLAG_ACCEPT_NEAR) != 0).sum()),
             "cdf_near": int(((f & oracle.FLAG_CDF_NEAR) != 0).sum()),
+            "s_near": int(((f & oracle.FLAG_S_NEAR) != 0).sum()),
             "topp_near": int(((f & oracle.FLAG_TOPP_NEAR) != 0).sum()),
             "topp_edge": int(((f & oracle.FLAG_TOPP_EDGE) != 0).sum()),
-            "excluded": int(((f & (oracle.FLAG_ACCEPT_NEAR | oracle.FLAG_CDF_NEAR)) != 0).sum()),
+            "excluded": int(((f & EXCLUDED) != 0).sum()),
             "requests": int(f.size)}
 
 
@@ -83,7 +89,8 @@ def check_sample(w, got, ref, requests=None):
       - accepted length and emitted token: equal to the defined outcome, or
         (a nucleus edge within 1e-6 of top_p) to one of the oracle's
         alternatives; requests whose uniform lies within 1e-6 relative of its
-        threshold or CDF step are left out and counted;
+        threshold or CDF step, or whose residual mass lies near the level
+        where the draw falls back to p', are left out and counted;
       - p'(x_i), q'(x_i): within 1e-5 of the defined or an alternative value,
         on every request;
       - S: within 1e-5 of the S of a variant with the GPU's accepted length;
@@ -94,7 +101,7 @@ def check_sample(w, got, ref, requests=None):
     acc = host(got["accepted"])[idx]
     tok = host(got["tokens"])[idx]
     flags = ref["flags"]
-    excluded = (flags & (oracle.FLAG_ACCEPT_NEAR | oracle.FLAG_CDF_NEAR)) != 0
+    excluded = (flags & EXCLUDED) != 0
     have_p = "p" in got
     if have_p:
         p = host(got["p"])[idx]

@@ -210,3 +210,34 @@ def test_flags_are_rare_on_the_reduced_workloads():
             total += w.B
             flagged += int(((f & oracle.FLAG_AMBIGUOUS) != 0).sum())
     assert flagged <= total // 50
+
+
+# ---------------------------------------------------------------------------
+# residual mass near the level below which the draw falls back to p'
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S_target,fallback,flagged", [
+    (2.0 ** -26, True, False), (0.5 * oracle.S_RESOLUTION, True, True),
+    (2.0 * oracle.S_RESOLUTION, False, True), (2.0 ** -16, False, False),
+])
+def test_small_residual_mass(S_target, fallback, flagged):
+    """p' = [2d, 1 - 3d, d] and q' = [d, 1 - 3d, 2d]: token 2 (ratio 1/2)
+    rejected at u = 3/4 leaves the residual [d, 0, 0], S = d.  At or below
+    2^-20 the draw takes p' (token 1 at u_sample = 1/2), above it the
+    residual (token 0); within a factor 4 of the level the request is
+    flagged."""
+    d = S_target
+    lt = np.log(np.array([2 * d, 1 - 3 * d, d])).astype(np.float32)
+    ld = np.log(np.array([d, 1 - 3 * d, 2 * d])).astype(np.float32)
+    p = special.softmax(lt.astype(np.float64))
+    q = special.softmax(ld.astype(np.float64))
+    S = np.maximum(p - q, 0.0).sum()
+    assert 0.5 < S / S_target < 2.0
+    out = run([lt, lt], [ld], [2], [0.75], 0.5)
+    assert out["accepted"][0] == 0
+    assert bool(out["flags"][0] & oracle.FLAG_FALLBACK) == fallback
+    assert bool(out["flags"][0] & oracle.FLAG_S_NEAR) == flagged
+    if fallback:
+        assert out["tokens"][0, 0] == 1 and out["S"][0] == pytest.approx(1.0, abs=1e-12)
+    else:
+        assert out["tokens"][0, 0] == 0 and out["S"][0] == pytest.approx(S, rel=1e-6)

@@ -366,12 +366,13 @@ def test_zero_residual_mass_draws_from_p(dtype):
     if dtype == "f32":
         w = W.sample_gaussian(32, 6, 8, 30011, "f32", 3.0, 0.5, 0.7, seed=7, name="p' draw f32")
     w.draft = w.target[:, :w.K].copy()
-    w.tokens = W.drafter_tokens(W.logits_as_f32(w.draft, dtype), w.temperature, 1.0,
-                                np.random.default_rng(2))
-    w.tokens[0, 0] = w.V
-    w.tokens[2, 3] = -1
-    w.tokens[5, 7] = w.V + 5
     for top_p in (1.0, float(np.float32(0.9))):
+        # tokens from the drafter's own nucleus: every in-range draft survives
+        w.tokens = W.drafter_tokens(W.logits_as_f32(w.draft, dtype), w.temperature, top_p,
+                                    np.random.default_rng(2))
+        w.tokens[0, 0] = w.V
+        w.tokens[2, 3] = -1
+        w.tokens[5, 7] = w.V + 5
         w.top_p = top_p
         got, ref = _check(w)
         for b, i in ((0, 0), (2, 3), (5, 7)):
