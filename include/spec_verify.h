@@ -42,7 +42,8 @@
  *    (-inf entries are allowed and have probability 0; NaN / +inf are not).
  *  - The caller owns every buffer.  The library never allocates or frees
  *    device memory and keeps no state between calls (outside the optional
- *    profiling hook below).  Inputs are read-only.
+ *    profiling hook below, and the one array per GPU that the loader places
+ *    in device memory for spec_verify_sample_noalloc).  Inputs are read-only.
  *  - `workspace` is caller-provided device scratch of at least
  *    spec_verify_workspace_bytes(...) bytes, 256-byte aligned.  It needs no
  *    clearing: every call tags what it writes there with fresh epoch bits.
@@ -118,6 +119,27 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
                        int B, int K, int V, int32_t *out_accepted, int32_t *out_tokens,
                        float *out_p_draft, float *out_q_draft, float *out_residual_mass,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* spec_verify_sample on a workspace the library holds, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Arguments, outputs and errors as
+ * spec_verify_sample, without workspace / workspace_bytes.  The workspace is
+ * one array of SPEC_SCRATCH_BYTES in device memory per GPU, held until the
+ * process ends; calls needing more (spec_verify_workspace_bytes(
+ * SPEC_OP_SAMPLE, ...) > SPEC_SCRATCH_BYTES) return SPEC_ERR_WORKSPACE with
+ * nothing enqueued.  The call allocates nothing.  Every call on one GPU uses
+ * that GPU's array: calls that may overlap on one GPU (other streams, other
+ * threads) race and must not be issued; calls in one stream are ordered and
+ * safe.  Nothing in the array needs clearing between calls (each call tags
+ * what it writes with fresh epoch bits).  The first call on a device looks
+ * up the array's address on that device (SPEC_ERR_HIP if that fails). */
+#define SPEC_SCRATCH_BYTES (32u << 20)
+int spec_verify_sample_noalloc(const void *target_logits, const void *draft_logits, int dtype,
+                               const int32_t *draft_tokens, const float *u_accept,
+                               const float *u_sample, float temperature, float top_p, int B,
+                               int K, int V, int32_t *out_accepted, int32_t *out_tokens,
+                               float *out_p_draft, float *out_q_draft,
+                               float *out_residual_mass, hipStream_t stream);
 
 /* Sampling verify with per-request temperature and top-p, greedy and
  * sampling requests mixed in one batch (temperature 0 is the greedy rule:

@@ -8,7 +8,8 @@ current HIP stream.  If the library has not been built the calls raise: there
 is no fallback implementation.
 
 Entry points (same names as the C ABI, minus the ``spec_`` prefix):
-``verify_greedy``, ``verify_sample``, ``verify_mixed``, ``verify_tree``, ``tree_merge``,
+``verify_greedy``, ``verify_sample``, ``verify_sample_noalloc``, ``verify_mixed``,
+``verify_tree``, ``tree_merge``,
 ``kv_commit``,
 ``verify_workspace_bytes``, ``status_string``, ``profile_begin``,
 ``profile_end``.
@@ -25,11 +26,12 @@ LIB_PATH = os.path.join(PKG, "libspecverify.so")
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_OP_GREEDY, SPEC_OP_SAMPLE, SPEC_OP_TREE = 0, 1, 2
 SPEC_OK = 0
+SPEC_SCRATCH_BYTES = 32 << 20  # the library-held workspace of spec_verify_sample_noalloc
 ERRORS = {-1: "SPEC_ERR_NULL", -2: "SPEC_ERR_SHAPE", -3: "SPEC_ERR_PARAM",
           -4: "SPEC_ERR_WORKSPACE", -5: "SPEC_ERR_ALIGN", -6: "SPEC_ERR_HIP"}
 
 EXPORTS = ("spec_verify_workspace_bytes", "spec_verify_greedy", "spec_verify_sample",
-           "spec_verify_mixed", "spec_verify_tree", "spec_tree_merge",
+           "spec_verify_sample_noalloc", "spec_verify_mixed", "spec_verify_tree", "spec_tree_merge",
            "spec_lmhead_greedy", "spec_lmhead_workspace_bytes", "spec_kv_commit", "spec_status_string", "spec_profile_begin",
            "spec_profile_end")
 
@@ -59,6 +61,8 @@ def load() -> ctypes.CDLL:
     L.spec_verify_greedy.restype = I
     L.spec_verify_sample.argtypes = [P, P, I, P, P, P, F, F, I, I, I, P, P, P, P, P, P, Z, P]
     L.spec_verify_sample.restype = I
+    L.spec_verify_sample_noalloc.argtypes = [P, P, I, P, P, P, F, F, I, I, I, P, P, P, P, P, P]
+    L.spec_verify_sample_noalloc.restype = I
     L.spec_verify_mixed.argtypes = [P, P, I, P, P, P, P, P, I, I, I, P, P, P, P, P, P, Z, P]
     L.spec_verify_mixed.restype = I
     L.spec_verify_tree.argtypes = [P, I, P, P, P, I, I, I, P, P, P, P, Z, P]
@@ -212,6 +216,35 @@ def verify_sample(target, draft, draft_tokens, u_accept, u_sample, temperature: 
         _ws_ptr(ws), _ws_avail(ws), _stream(dev, stream))
     if rc != SPEC_OK:
         raise SpecVerifyError(rc, "spec_verify_sample")
+    return out
+
+
+def verify_sample_noalloc(target, draft, draft_tokens, u_accept, u_sample, temperature: float,
+                          top_p: float = 1.0, *, out, stream=None) -> Dict[str, object]:
+    """verify_sample on the library's own workspace (spec_verify_sample_noalloc):
+    nothing is allocated, by the library or here; `out` holds the caller's
+    output tensors (accepted, tokens and optionally p, q, residual_mass)."""
+    torch = _torch()
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    _check(target, "target", (B, K1, V), device=dev)
+    _check(draft, "draft", (B, K, V), target.dtype, dev)
+    _check(draft_tokens, "draft_tokens", (B, K), torch.int32, dev)
+    _check(u_accept, "u_accept", (B, K), torch.float32, dev)
+    _check(u_sample, "u_sample", (B,), torch.float32, dev)
+    _check(out["accepted"], "out accepted", (B,), torch.int32, dev)
+    _check(out["tokens"], "out tokens", (B, K1), torch.int32, dev)
+    for name, shape in (("p", (B, K)), ("q", (B, K)), ("residual_mass", (B,))):
+        if out.get(name) is not None:
+            _check(out[name], f"out {name}", shape, torch.float32, dev)
+    rc = load().spec_verify_sample_noalloc(
+        _ptr(target), _ptr(draft), _logit_dtype(target), _ptr(draft_tokens), _ptr(u_accept),
+        _ptr(u_sample), float(temperature), float(top_p), B, K, V, _ptr(out["accepted"]),
+        _ptr(out["tokens"]), _ptr(out.get("p")), _ptr(out.get("q")),
+        _ptr(out.get("residual_mass")), _stream(dev, stream))
+    if rc != SPEC_OK:
+        raise SpecVerifyError(rc, "spec_verify_sample_noalloc")
     return out
 
 

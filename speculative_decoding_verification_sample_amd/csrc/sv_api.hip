@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "spec_verify.h"
@@ -227,6 +228,62 @@ int spec_verify_sample(const void *target_logits, const void *draft_logits, int 
   return run_sample(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample, k64,
                     top_p, nullptr, nullptr, B, K, V, out_accepted, out_tokens, out_p_draft,
                     out_q_draft, out_residual_mass, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the sampling call on a library-held workspace ----
+// One array per GPU, in device memory, for callers that cannot allocate.
+// In host code `scratch` names a host-side stand-in, not a device address:
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[SPEC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (its device address); looked up on
+// the first call on that device.
+int scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPEC_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_sample_noalloc(const void *target_logits, const void *draft_logits, int dtype,
+                               const int32_t *draft_tokens, const float *u_accept,
+                               const float *u_sample, float temperature, float top_p, int B,
+                               int K, int V, int32_t *out_accepted, int32_t *out_tokens,
+                               float *out_p_draft, float *out_q_draft,
+                               float *out_residual_mass, hipStream_t stream) {
+  int rc = check_sample_args(target_logits, draft_logits, dtype, draft_tokens, u_accept,
+                             u_sample, B, K, V, out_accepted, out_tokens);
+  if (rc) return rc;
+  if (!std::isfinite(temperature) || !(temperature > 0.0f)) return SPEC_ERR_PARAM;
+  if (!(top_p > 0.0f) || !(top_p <= 1.0f)) return SPEC_ERR_PARAM;
+  const double k64 = sv::kLog2e / (double)temperature;
+  if (!std::isfinite(k64) || !(k64 > 0.0) || k64 > 3.0e38) return SPEC_ERR_PARAM;
+  const Layout L = sv::make_layout(SPEC_OP_SAMPLE, B, K, V, dtype, top_p < 1.0f);
+  if (L.total > (size_t)SPEC_SCRATCH_BYTES) return SPEC_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return run_sample(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample, k64,
+                    top_p, nullptr, nullptr, B, K, V, out_accepted, out_tokens, out_p_draft,
+                    out_q_draft, out_residual_mass, ws, (size_t)SPEC_SCRATCH_BYTES, stream);
 }
 
 int spec_verify_mixed(const void *target_logits, const void *draft_logits, int dtype,

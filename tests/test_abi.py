@@ -182,3 +182,36 @@ def test_lmhead_errors():
     assert call(B=0) == -2 and call(V=0) == -2
     assert call(h=FAKE + 8) == -5 and call(ws=FAKE + 64) == -5
     assert call(wsb=10) == -4
+
+
+def _sample_noalloc(**kw):
+    args = dict(t=FAKE, d=FAKE, dt=0, tok=FAKE, ua=FAKE, us=FAKE, T=1.0, top_p=1.0, B=2, K=3,
+                V=100, acc=FAKE, out=FAKE, p=None, q=None, S=None, stream=None)
+    args.update(kw)
+    a = args
+    return sv.load().spec_verify_sample_noalloc(a["t"], a["d"], a["dt"], a["tok"], a["ua"],
+                                                a["us"], a["T"], a["top_p"], a["B"], a["K"],
+                                                a["V"], a["acc"], a["out"], a["p"], a["q"],
+                                                a["S"], a["stream"])
+
+
+def test_noalloc_host_errors():
+    """Invalid arguments of the no-allocation call return their codes before
+    any HIP call, as the workspace-taking call does; a call whose workspace
+    would exceed the library's array returns SPEC_ERR_WORKSPACE."""
+    assert _sample_noalloc(t=None) == -1
+    assert _sample_noalloc(us=None) == -1
+    assert _sample_noalloc(dt=7) == -3
+    assert _sample_noalloc(T=0.0) == -3
+    assert _sample_noalloc(T=float("nan")) == -3
+    assert _sample_noalloc(top_p=0.0) == -3
+    assert _sample_noalloc(top_p=1.5) == -3
+    assert _sample_noalloc(K=64) == -2
+    assert _sample_noalloc(B=0) == -2
+    assert _sample_noalloc(t=FAKE + 2) == -5
+    # sizes: the headline fits; top-p at the large-batch setting does not
+    need = sv.verify_workspace_bytes(sv.SPEC_OP_SAMPLE, 64, 8, 128256, sv.SPEC_BF16, False)
+    assert 0 < need <= sv.SPEC_SCRATCH_BYTES
+    big = sv.verify_workspace_bytes(sv.SPEC_OP_SAMPLE, 256, 4, 152064, sv.SPEC_F32, True)
+    assert big > sv.SPEC_SCRATCH_BYTES
+    assert _sample_noalloc(B=256, K=4, V=152064, top_p=0.95) == -4
