@@ -174,6 +174,9 @@ int run_sample(const void *target_logits, const void *draft_logits, int dtype,
   a.band_n = use_top_p ? carve<unsigned>(workspace, L.band_n) : nullptr;
   a.band_keys = use_top_p ? carve<uint32_t>(workspace, L.band_keys) : nullptr;
   a.band_above = use_top_p ? carve<double>(workspace, L.band_above) : nullptr;
+  // top-p with batch-wide parameters: the ratio tests once per request, in
+  // their own launch before the residual tiles
+  a.dec = use_top_p && temps == nullptr ? carve<sv::Decision>(workspace, L.dec) : nullptr;
   a.out_accepted = out_accepted;
   a.out_tokens = out_tokens;
   a.out_p = out_p_draft;
@@ -188,6 +191,12 @@ int run_sample(const void *target_logits, const void *draft_logits, int dtype,
   prof_after(stream);
   if (use_top_p) {
     if (sv::launch_topp_select(a, dtype, stream) != hipSuccess) return SPEC_ERR_HIP;
+    if (a.dec) {  // batch-wide parameters: decide, residual masses, draw
+      if (sv::launch_topp_decide(a, stream) != hipSuccess ||
+          sv::launch_topp_residual(a, dtype, stream) != hipSuccess)
+        return SPEC_ERR_HIP;
+      return SPEC_OK;
+    }
     a.phase = 2;
     if (sv::launch_sample(a, dtype, stream) != hipSuccess) return SPEC_ERR_HIP;
   }

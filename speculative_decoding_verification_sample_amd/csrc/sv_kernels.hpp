@@ -21,6 +21,13 @@ hipError_t launch_tree(const void *target, int dtype, const int32_t *parents,
 // 1 = streaming tiles only, 2 = residual tiles only (around the top-p kernel)
 hipError_t launch_sample(const SampleArgs &args, int dtype, hipStream_t stream);
 
+// the ratio tests of a top-p call with batch-wide parameters, once per
+// request, after the nucleus launches (sv_sample.hip)
+hipError_t launch_topp_decide(const SampleArgs &args, hipStream_t stream);
+// ... then the residual masses of the drawn row pairs and the draw, in two
+// launches that never wait on each other's workgroups (sv_sample.hip)
+hipError_t launch_topp_residual(const SampleArgs &args, int dtype, hipStream_t stream);
+
 // workgroups of the fused sampling kernel resident at once (cached per dtype)
 int resident_workgroups(int dtype);
 

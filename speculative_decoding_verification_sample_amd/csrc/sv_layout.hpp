@@ -145,6 +145,9 @@ struct SampleArgs {
   unsigned *band_n;  // top-p: per row, keys in the band (the list holds the first kBandKeys)
   uint32_t *band_keys;  // top-p: per row, kBandKeys keys
   double *band_above;   // top-p: per row, exact mass above the band
+  Decision *dec;        // top-p, batch-wide parameters: per request, the outcome of the
+                        // ratio tests, decided once before the residual tiles (n = -1:
+                        // the request failed)
   int32_t *out_accepted, *out_tokens;
   float *out_p, *out_q, *out_mass;
 };
@@ -191,6 +194,7 @@ struct Layout {
   int rows = 0;    // logit rows streamed
   size_t part_m = 0, part_z = 0, part_x = 0, part_key = 0, part_tag = 0, rowstat = 0;
   size_t rtot = 0, part_h = 0, part_c = 0, topband = 0, band_n = 0, band_keys = 0, band_above = 0;
+  size_t dec = 0;
   // sampling: part_m one self-validating u64 word per (row, split) (the split
   // maximum), part_z two (the split mass as fp32 hi + lo);
   // part_x one word per (request, position, target / draft): the logit of the
@@ -231,6 +235,7 @@ inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p
       L.band_n = take((size_t)L.rows * sizeof(unsigned));
       L.band_keys = take((size_t)L.rows * kBandKeys * sizeof(uint32_t));
       L.band_above = take((size_t)L.rows * sizeof(double));
+      L.dec = take((size_t)B * sizeof(Decision));
     }
   } else {
     L.part_key = take(cells * sizeof(uint64_t));

@@ -973,6 +973,177 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
                              a.out_mass, b, idx, rl);
 }
 
+// The ratio tests of a top-p call with batch-wide parameters, one workgroup
+// per request, between the nucleus launches and the residual tiles: the
+// outcome, the emitted drafts and the per-position probabilities are
+// written here once, and the residual tiles read the request's Decision
+// instead of each deciding again.
+__global__ __launch_bounds__(kThreads) void k_topp_decide(SampleArgs a) {
+  __shared__ DecideLds lds;
+  __shared__ Decision sdec;
+  __shared__ int s_ok;
+  const int b = (int)blockIdx.x;
+  if (!decide(a.tokens, a.u_accept, a.B, a.K, a.S, a.k64, a.k, a.part_m, a.part_z, a.part_x,
+              a.epoch, a.rowstat, b, true, a.out_accepted, a.out_tokens, a.out_p, a.out_q, lds,
+              &sdec, &s_ok)) {
+    if (threadIdx.x == 0) {
+      a.out_accepted[b] = -2;  // time-out: flag the request as failed
+      Decision d = {};
+      d.n = -1;
+      a.dec[b] = d;
+    }
+    return;
+  }
+  if (threadIdx.x == 0) a.dec[b] = sdec;
+}
+
+hipError_t launch_topp_decide(const SampleArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL(k_topp_decide, dim3(a.B), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// After the decide launch of a top-p call: the residual (or bonus) mass of
+// every residual split of each request's drawn row pair, one workgroup per
+// (request, split), stored as a plain fp64 value for the draw launch.  No
+// workgroup waits for another: the launch streams at the memory's pace.
+constexpr int kMassSplits = 2;  // residual splits per workgroup of the mass launch
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_resid_mass(SampleArgs a) {
+  __shared__ double red[kThreads / 64];
+  __shared__ double eh[kMassSplits], et[kMassSplits];
+  const int per_req = (a.SB + kMassSplits - 1) / kMassSplits;
+  const int b = (int)blockIdx.x / per_req;
+  const int s0 = ((int)blockIdx.x - b * per_req) * kMassSplits;
+  const Decision d = a.dec[b];
+  if (d.n < 0) return;
+  const char *rt = row_ptr(a.target, (size_t)b * (a.K + 1) + d.n, a.V, DT);
+  const char *rd = d.mode == kModeResidual ? row_ptr(a.draft, (size_t)b * a.K + d.n, a.V, DT) : rt;
+  // every split's loads issued before any is used
+  SplitGeo g[kMassSplits];
+  LaneGroups mine[kMassSplits];
+#pragma unroll
+  for (int j = 0; j < kMassSplits; ++j) {
+    g[j] = split_geo<DT>(rt, rd, a.V, min(s0 + j, a.SB - 1));
+    load_lane<DT, false>(g[j], mine[j]);
+  }
+  if (threadIdx.x < kMassSplits && s0 + (int)threadIdx.x < a.SB) {
+    const int j = threadIdx.x;
+    const SplitGeo gj = split_geo<DT>(rt, rd, a.V, s0 + j);
+    eh[j] = range_mass<DT, true, false>(gj, 0, gj.head, d, a.k);
+    et[j] = range_mass<DT, true, false>(gj, gj.tail0, gj.n, d, a.k);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kMassSplits; ++j) {
+    if (s0 + j >= a.SB) break;
+    const double lm = lane_mass<DT, true, false>(g[j], mine[j], d, a.k);
+    const double tot = block_sum(lm + (threadIdx.x == 0 ? eh[j] + et[j] : 0.0), red);
+    if (threadIdx.x == 0)
+      reinterpret_cast<double *>(a.rtot)[(size_t)b * a.SB + s0 + j] = tot;
+  }
+}
+
+// The draw of a top-p call, one workgroup per request: the split where the
+// cumulative residual mass passes u * S (from the split masses of the mass
+// launch), then that split of the row pair read again and scanned; if the
+// residual mass is not above the resolution level, the draw from p' instead
+// (every split's p' mass, then the same steps).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_resid_draw(SampleArgs a) {
+  __shared__ DrawLds D;
+  __shared__ double red[kThreads / 64];
+  __shared__ int s_split;
+  __shared__ double s_rem, s_total;
+  const int t = threadIdx.x, b = (int)blockIdx.x, SB = a.SB, K = a.K;
+  const Decision d = a.dec[b];
+  if (d.n < 0) return;
+  const char *rt = row_ptr(a.target, (size_t)b * (K + 1) + d.n, a.V, DT);
+  const char *rd = d.mode == kModeResidual ? row_ptr(a.draft, (size_t)b * K + d.n, a.V, DT) : rt;
+  const float us = a.u_sample[b];
+  const double *tot = reinterpret_cast<const double *>(a.rtot) + (size_t)b * SB;
+  for (int i = t; i < SB; i += kThreads) D.tot[i] = tot[i];
+  __syncthreads();
+  if (SB <= 64) {
+    if (t < 64) {
+      double rem, total;
+      const int split = pick_split_wave(t < SB ? D.tot[t] : 0.0, SB, us, &rem, &total);
+      if (t == 0) {
+        s_split = split;
+        s_rem = rem;
+        s_total = total;
+      }
+    }
+  } else if (t == 0) {
+    double rem, total;
+    s_split = pick_split(D.tot, SB, us, &rem, &total);
+    s_rem = rem;
+    s_total = total;
+  }
+  __syncthreads();
+  const bool use_p = !(s_total > kResidualResolution);
+  if (use_p) {  // S = 0 in exact arithmetic: p' of every split, then the pick again
+    for (int i = 0; i < SB; ++i) {
+      const SplitGeo gi = split_geo<DT>(rt, rd, a.V, i);
+      LaneGroups li;
+      load_lane<DT, true>(gi, li);
+      double v = lane_mass<DT, true, true>(gi, li, d, a.k);
+      if (t == 0)
+        v += range_mass<DT, true, true>(gi, 0, gi.head, d, a.k) +
+             range_mass<DT, true, true>(gi, gi.tail0, gi.n, d, a.k);
+      v = block_sum(v, red);
+      if (t == 0) D.tot[i] = v;
+    }
+    __syncthreads();
+    if (t == 0) {
+      double rem, total;
+      s_split = pick_split(D.tot, SB, us, &rem, &total);
+      s_rem = rem;
+      s_total = total;
+    }
+    __syncthreads();
+  }
+  int tok = -1;
+  const int split = s_split;
+  if (split >= 0) {
+    const SplitGeo g = split_geo<DT>(rt, rd, a.V, split);
+    LaneGroups mine;
+    if (use_p) load_lane<DT, true>(g, mine);
+    else load_lane<DT, false>(g, mine);
+    const double el = use_p ? lane_mass<DT, true, true>(g, mine, d, a.k)
+                            : lane_mass<DT, true, false>(g, mine, d, a.k);
+    if (t == 0) {
+      D.eh = use_p ? range_mass<DT, true, true>(g, 0, g.head, d, a.k)
+                   : range_mass<DT, true, false>(g, 0, g.head, d, a.k);
+      D.et = use_p ? range_mass<DT, true, true>(g, g.tail0, g.n, d, a.k)
+                   : range_mass<DT, true, false>(g, g.tail0, g.n, d, a.k);
+    }
+    __syncthreads();
+    const double eh = D.eh, et = D.et;
+    const SplitScan sc = scan_split(eh, el, D);
+    const int local = use_p ? draw_split<DT, true, true>(g, eh, el, et, sc, s_rem, d, a.k, D)
+                            : draw_split<DT, true, false>(g, eh, el, et, sc, s_rem, d, a.k, D);
+    if (local >= 0) tok = g.e0 + local;
+  }
+  if (t == 0) {
+    a.out_tokens[(size_t)b * (K + 1) + d.n] = tok;
+    if (a.out_mass) a.out_mass[b] = (float)s_total;
+  }
+}
+
+hipError_t launch_topp_residual(const SampleArgs &a, int dtype, hipStream_t stream) {
+  if (dtype == kBF16) {
+    hipLaunchKernelGGL(k_resid_mass<kBF16>, dim3(a.B * ((a.SB + kMassSplits - 1) / kMassSplits)),
+                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_resid_draw<kBF16>, dim3(a.B), dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(k_resid_mass<kF32>, dim3(a.B * ((a.SB + kMassSplits - 1) / kMassSplits)),
+                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(k_resid_draw<kF32>, dim3(a.B), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_sample(const SampleArgs &args, int dtype, hipStream_t stream) {
   SampleArgs a = args;
   const int nA = a.B * (2 * a.K + 1) * a.S;
