@@ -59,6 +59,11 @@ def _code_only(text: str) -> str:
 KERNEL_SOURCES = {
     "k_sample_fused": ("sv_sample.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
     "k_topp_gather": ("sv_topp.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
+    "k_topp_band": ("sv_topp.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
+    "k_topp_cut": ("sv_topp.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
+    "k_topp_decide": ("sv_sample.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
+    "k_resid_mass": ("sv_sample.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
+    "k_resid_draw": ("sv_sample.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
     "k_argmax_fused": ("sv_stream.hip", "sv_tiles.hpp", "sv_device.hpp", "sv_layout.hpp"),
     "k_kv_commit": ("sv_kv.hip", "sv_device.hpp", "sv_layout.hpp"),
     "k_tree_merge": ("sv_merge.hip", "sv_device.hpp", "sv_layout.hpp"),
