@@ -105,7 +105,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--min-warmup-s", type=float, default=0.3,
                     help="keep warming up until this many seconds have passed")
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["kv", "merge", "lmhead"],
+    ap.add_argument("--workload", default="c3",
+                    choices=sorted(WORKLOADS) + ["kv", "merge", "lmhead", "lmhead_sample"],
                     help="c1..c5: the five settings; mixed: the headline inputs with "
                          "per-request temperatures; kv: the KV-cache commit; "
                          "merge: two drafters' trees merged with confidence routing; "
@@ -118,11 +119,12 @@ def main():
                     help="only run a plain device copy of this many MiB, 20 times (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
-    if args.workload in ("kv", "merge", "lmhead"):
+    if args.workload in ("kv", "merge", "lmhead", "lmhead_sample"):
         if args.gpus != 1:
             print("bench.py: one GPU only", file=sys.stderr)
             sys.exit(2)
-        {"kv": kv_bench, "merge": merge_bench, "lmhead": lmhead_bench}[args.workload](args)
+        {"kv": kv_bench, "merge": merge_bench, "lmhead": lmhead_bench,
+         "lmhead_sample": lmhead_sample_bench}[args.workload](args)
         return
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
@@ -483,7 +485,11 @@ def lmhead_bench(args):
     M = B * (K + 1)
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
     hid, wgt = up(wl.hidden), up(wl.weight)
-    tok = torch.from_numpy(wl.tokens).to(dev)
+    # draft tokens drawn from the drafter's own distribution (as a drafter
+    # does), so that the residual mass is never negligible by construction
+    probs = torch.softmax(draft.float().view(B * K, V) / T, dim=-1)
+    tok = torch.multinomial(probs, 1, generator=g).view(B, K).to(torch.int32)
+    del probs
     ws = torch.empty(sv.load().spec_lmhead_workspace_bytes(B, K, d, V) + 256, dtype=torch.uint8,
                      device=dev)
     out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
@@ -556,6 +562,95 @@ def lmhead_bench(args):
         "unfused": {"us_per_step": ums * 1000.0,
                     "what": "torch.mm bf16 logits [M, V] (hipBLASLt) + spec_verify_greedy"},
         "cpu_baseline": cpu}), flush=True)
+
+
+def lmhead_sample_bench(args):
+    """What fusing the LM head in front of sampling verification could save,
+    measured at the sampling workload's shape: B=64 requests of K=8 drafts (576 target
+    positions), hidden size 4096, V=128256, bf16, T=0.7.  Timed on the same
+    inputs: (1) torch's bf16 matmul writing the target logits (hipBLASLt);
+    (2) spec_verify_sample on those logits and draft logits (the unfused
+    path is 1 + 2); (3) the library's matrix-core pass over the vocabulary
+    matrix with a per-row reduction epilogue (spec_lmhead_greedy at this
+    shape), the floor of any fused front end, which would still have to
+    stream the draft rows and re-read the drawn row pairs and would add an
+    exponential per logit to its epilogue; (4) the target rows' share of
+    the verify's streamed bytes at the verify's own rate, the most a fused
+    front end could take off (2)."""
+    import numpy as np
+    import torch
+
+    import speculative_decoding_verification_sample_amd as sv
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    B, K, T = 64, 8, 0.7
+    wl = W.lmhead_workload(seed=0, B=B, K=K)
+    d, V = wl.d, wl.V
+    M = B * (K + 1)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    hid, wgt = up(wl.hidden), up(wl.weight)
+    hb, wb = hid.view(torch.bfloat16).view(M, d), wgt.view(torch.bfloat16)
+    logits = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+    torch.mm(hb, wb.t(), out=logits)
+    g = torch.Generator(device=dev).manual_seed(5)
+    draft = (logits.view(B, K + 1, V)[:, :K].float()
+             + 0.5 * torch.randn((B, K, V), generator=g, device=dev)).to(torch.bfloat16)
+    # draft tokens drawn from the drafter's own distribution (as a drafter
+    # does), so that the residual mass is never negligible by construction
+    probs = torch.softmax(draft.float().view(B * K, V) / T, dim=-1)
+    tok = torch.multinomial(probs, 1, generator=g).view(B, K).to(torch.int32)
+    del probs
+    ua = torch.rand((B, K), generator=g, device=dev)
+    us = torch.rand((B,), generator=g, device=dev)
+    tgt16, dft16 = logits.view(torch.int16).view(B, K + 1, V), draft.view(torch.int16)
+    ws = torch.empty(sv.verify_workspace_bytes(sv.SPEC_OP_SAMPLE, B, K, V, sv.SPEC_BF16) + 256,
+                     dtype=torch.uint8, device=dev)
+    out = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+               tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+    lws = torch.empty(sv.load().spec_lmhead_workspace_bytes(B, K, d, V) + 256, dtype=torch.uint8,
+                      device=dev)
+    gout = dict(accepted=torch.empty(B, dtype=torch.int32, device=dev),
+                tokens=torch.empty((B, K + 1), dtype=torch.int32, device=dev))
+
+    def timed(fn, steps):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.min_warmup_s:
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / steps
+
+    steps = max(20, args.steps)
+    ver = lambda: sv.verify_sample(tgt16, dft16, tok, ua, us, T, 1.0, diagnostics=False,
+                                   workspace=ws, out=out)
+    ver_us = timed(ver, steps)
+    mm_us = timed(lambda: torch.mm(hb, wb.t(), out=logits), steps)
+    unfused_us = timed(lambda: (torch.mm(hb, wb.t(), out=logits), ver()), steps)
+    fused_gemm_us = timed(lambda: sv.lmhead_greedy(hid, wgt, tok, workspace=lws, out=gout), steps)
+    share = (K + 1) / (2 * K + 1)
+    print(json.dumps({
+        "metric": "LM head + sampling verify: unfused path and the fused bound, us per call",
+        "value": unfused_us, "unit": "us", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": unfused_us / 1000.0, "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (random weights)",
+        "config": {"workload": f"lmhead + sample B{B} K{K} d{d} V{V} bf16 T{T}",
+                   "parallelism": "none (1 GPU)"},
+        "torch_mm_logits_us": mm_us, "verify_sample_us": ver_us, "unfused_us": unfused_us,
+        "matrix_core_pass_us": fused_gemm_us,
+        "target_rows_share_of_verify_us": share * ver_us,
+        "fused_bound_us": fused_gemm_us + (1 - share) * ver_us,
+        "note": "fused_bound = the library's matrix-core pass at this shape + the verify's "
+                "draft-row share; a fused front end would also re-read the drawn row pairs "
+                "and add an exponential per logit, so this bound is optimistic"}), flush=True)
 
 
 def copy_probe(mib):

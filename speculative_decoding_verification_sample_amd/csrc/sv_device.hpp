@@ -126,6 +126,15 @@ __device__ __forceinline__ float f32_of_key(uint32_t k) {
 
 __device__ __forceinline__ float exp2_fast(float a) { return __builtin_amdgcn_exp2f(a); }
 
+// floor(x) as a signed integer in one instruction (v_cvt_flr_i32_f32, which
+// the compiler does not form from floorf and a conversion): exact for |x| <
+// 2^31, saturating beyond (-inf gives INT_MIN), NaN gives 0.
+__device__ __forceinline__ int floor_to_int(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
 // The upper 16 bits of x's fp32 pattern, raised by one unit where that is
 // needed for the value they denote (low bits zero) not to lie below x:
 // positive x with nonzero low bits.  NaN gives +inf.

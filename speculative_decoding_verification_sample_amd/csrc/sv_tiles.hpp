@@ -135,13 +135,17 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
     for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, sm[w]);
     if (M > -INFINITY) {
       const float kk = (k.hi + k.lo) * kHistPerLog2;
-      const float F = floorf(M * kk);
-      // branch-free: an element past the counted bins (or -inf) adds to
-      // its lane's spare slot instead (distinct per lane: no conflicts)
-      const int spare = kHistBins + lane_id();
+      // F = floor(M kk) as an integer: |M kk| < 2^31 wherever the counts are
+      // used (the band launch requires |M kk| < 2^18)
+      const unsigned F = (unsigned)floor_to_int(M * kk);
+      // branch-free: j = F - floor(x kk) >= 0 (x <= M) in unsigned
+      // arithmetic; -inf (INT_MIN) and everything past the counted bins give
+      // j >= kHistBins, which the minimum sends to a spare slot beyond the
+      // bins (the lane's own, or one of a lane below: never read back)
+      const unsigned spare = kHistBins + lane_id();
       auto count = [&](float x) {
-        const float j = F - floorf(x * kk);  // >= 0: x <= M; +inf for x = -inf
-        atomicAdd(&sh_hist[j < (float)kHistBins ? (int)j : spare], 1u);
+        const unsigned j = F - (unsigned)floor_to_int(x * kk);
+        atomicAdd(&sh_hist[min(j, spare)], 1u);
       };
 #pragma unroll
       for (int u = 0; u < kVecPerThread; ++u)

@@ -336,6 +336,13 @@ constexpr int kGRounds = kGWinEnt / (8 * kTopThreads);  // 16-byte loads of entr
 // 95, and the bf16 top-p call ran 577 -> 564 us at B256 K4 V152064)
 template <int DT>
 constexpr int gather_slots() { return DT == kBF16 ? 2 : 8; }
+constexpr int kGQueue = 256;     // vectors queued per wave before they are classified
+constexpr int kGWaveKeys = 256;  // band keys a wave holds per pass
+
+// rank of the calling lane among the lanes set in `bal` below it
+__device__ __forceinline__ unsigned lane_rank(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
 
 // Exclusive prefix of v over the workgroup; *total gets the sum.  Whole
 // workgroup; wtot is free again on return.
@@ -389,10 +396,16 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_gather(SampleArgs a) {
   __shared__ uint16_t list[kGWinEnt];
   __shared__ int wtot[kTopWaves];
   __shared__ double wsum[kTopWaves];
+  __shared__ u32x4 gq[kTopWaves][kGQueue];         // per wave: queued vectors
+  __shared__ uint32_t gkeys[kTopWaves][kGWaveKeys];  // per wave: the pass's band keys
+  __shared__ int gkn[kTopWaves];
+  const int w = t >> 6, lane = t & 63;
   uint32_t *keys = a.band_keys + (size_t)row * kBandKeys;
   const uint16_t *cm = a.part_c + (size_t)row * S * kChunksPerSplit;
   double above = 0.0;
   int kbase = 0;  // keys of the passes before (uniform)
+  int kn = 0;     // the wave's band keys in this pass (uniform in the wave)
+  bool lost = false;
   // split bodies: splits start 32 KB apart, so every full split has the
   // first one's head and vector count; the last has its own count
   const Span sp0 = split_span(tr.rp, a.V, 0, DT), spl = split_span(tr.rp, a.V, S - 1, DT);
@@ -465,38 +478,68 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_gather(SampleArgs a) {
             buf[r] = load_stream(body0 + (size_t)sp * kSplitVecs + v);
         }
       }
-      const float xp = p0 == 0 ? xs : -INFINITY;
-      int nb = 0;
-      auto visit = [&](float x) {
-        const float y = x * kk;
-        if (y >= yb) {
-          if (y >= ya) above += (double)tempered(x, M, k);
-          else ++nb;
+      // A listed line holds about one element at or above the band in
+      // thirty-two, scattered over the lanes, so classifying every element
+      // in place would run the mass and key code for nearly every element
+      // with a lane or two active.  Instead each wave first queues, in LDS,
+      // the vectors whose maximum reaches the band (one product and one
+      // compare per vector), then classifies the queue with every lane busy.
+      int qn = 0;  // queued vectors (uniform in the wave)
+      auto drain = [&]() {
+        for (int i0 = 0; i0 < qn; i0 += 64) {
+          const int i = i0 + lane;
+          const u32x4 v = i < qn ? gq[w][i] : neg_inf_vec<DT>();
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const float x = vec_elem(v, e, DT);
+            const float y = x * kk;
+            if (y >= ya) above += (double)tempered(x, M, k);
+            const bool inb = y >= yb && y < ya;
+            const uint64_t bal = __ballot(inb);
+            const int pos = kn + (int)lane_rank(bal);
+            if (inb && pos < kGWaveKeys) gkeys[w][pos] = key_of_f32(x);
+            kn += __popcll(bal);
+          }
         }
+        qn = 0;
+      };
+      auto push = [&](const u32x4 &v, float vmax) {
+        if (qn > kGQueue - 64) drain();
+        const bool hit = vmax * kk >= yb;
+        const uint64_t bal = __ballot(hit);
+        if (hit) gq[w][qn + (int)lane_rank(bal)] = v;
+        qn += __popcll(bal);
       };
 #pragma unroll
-      for (int r = 0; r < kGSlots; ++r)
+      for (int r = 0; r < kGSlots; ++r) {
+        float vmax = vec_elem(buf[r], 0, DT);
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) visit(vec_elem(buf[r], e, DT));
-      visit(xp);
-      int tot;
-      const int before = block_excl_scan(nb, wtot, &tot);
-      if (nb) {
-        unsigned slot = (unsigned)(kbase + before);
-        auto put = [&](float x) {
-          const float y = x * kk;
-          if (y >= yb && y < ya) {
-            if (slot < (unsigned)kBandKeys) keys[slot] = key_of_f32(x);
-            ++slot;
-          }
-        };
-#pragma unroll
-        for (int r = 0; r < kGSlots; ++r)
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) put(vec_elem(buf[r], e, DT));
-        put(xp);
+        for (int e = 1; e < EPV; ++e) vmax = fmaxf(vmax, vec_elem(buf[r], e, DT));
+        push(buf[r], vmax);
       }
+      if (p0 == 0) {  // the splits' scalar elements, as vectors of one element
+        u32x4 v = neg_inf_vec<DT>();
+        v[0] = DT == kBF16 ? (v[0] & 0xFFFF0000u) | (__float_as_uint(xs) >> 16) : __float_as_uint(xs);
+        push(v, xs);
+      }
+      drain();
+      // the wave's band keys of this pass go to the row's list after the
+      // keys of the waves before it (workgroup order: the same on every run)
+      if (lane == 0) gkn[w] = kn;
+      __syncthreads();
+      int off = kbase, tot = 0;
+#pragma unroll
+      for (int u = 0; u < kTopWaves; ++u) {
+        const int c = gkn[u];
+        off += u < w ? c : 0;
+        tot += c;
+        lost |= c > kGWaveKeys;
+      }
+      for (int i = lane; i < min(kn, kGWaveKeys); i += 64)
+        if (off + i < kBandKeys) keys[off + i] = gkeys[w][i];
       kbase += tot;
+      kn = 0;
+      __syncthreads();  // the queue and key lists are refilled by the next pass
     }
     __syncthreads();  // the list and split table are rewritten by the next window
   }
@@ -508,7 +551,9 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_gather(SampleArgs a) {
 #pragma unroll
     for (int u = 0; u < kTopWaves; ++u) sum += wsum[u];
     a.band_above[row] = sum;
-    a.band_n[row] = (unsigned)kbase;
+    // a wave that found more band keys in one pass than its LDS list holds
+    // dropped some: the cut then reads the row instead of the list
+    a.band_n[row] = lost ? (unsigned)max(kbase, kBandKeys + 1) : (unsigned)kbase;
   }
 }
 
