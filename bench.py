@@ -222,21 +222,25 @@ def main():
 
     # the streaming kernel alone: when a step is that one launch, the timed
     # region above is its duration (an upper bound: it includes the gaps
-    # between launches); otherwise (top-p: three launches per step) a second
-    # loop brackets each streaming launch with HIP events (which themselves
-    # add about a microsecond to what they bracket)
+    # between launches); otherwise (top-p: the streaming launch of each chunk
+    # of requests, then the top-p and residual launches) a second loop
+    # brackets each streaming launch with HIP events (which themselves add
+    # about a microsecond to what they bracket)
     single_launch = not (w0.kind == "sample" and w0.top_p < 1.0)
+    launches_per_call = 1
     if single_launch:
         kern_us = 1000.0 * total_ms / args.steps
         kern_src = "timed region / steps"
     else:
         n_iso = min(args.steps, 50)
-        sv.profile_begin(n_iso)
+        sv.profile_begin(8 * n_iso)
         for i in range(n_iso):
             calls[i % len(calls)]()
         kern_ms, launches = sv.profile_end()
+        launches_per_call = max(1, launches // n_iso)
         kern_us = 1000.0 * kern_ms / max(1, launches)
-        kern_src = f"HIP events around each streaming launch, {launches} launches"
+        kern_src = (f"HIP events around each streaming launch, {launches} launches "
+                    f"({launches_per_call} per call, one per chunk of requests)")
 
     # per-call distribution: each call bracketed by its own pair of events
     n_call = min(args.steps, 100)
@@ -272,7 +276,8 @@ def main():
         resample_bytes = int(sum(0 if g else (row if n == w0.K else 2 * row)
                                  for n, g in zip(acc, greedy_req)))
     kernel = "k_sample_fused" if w0.kind == "sample" else "k_argmax_fused"
-    achieved = algo_bytes / (kern_us * 1e-6) / 1e9
+    algo_launch = algo_bytes / launches_per_call  # the chunks are of equal size
+    achieved = algo_launch / (kern_us * 1e-6) / 1e9
     step_gbs = algo_bytes / (ms_per_step * 1e-3) / 1e9
     cpu = cpu_baseline(w0, args.cpu_seconds) if args.cpu_seconds > 0 else None
     outcomes = {}
@@ -306,8 +311,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "traffic_over_algorithmic": (traffic / algo_bytes) if traffic else None,
+                     "traffic_over_algorithmic": (traffic / algo_launch) if traffic else None,
                      "kernel_us": kern_us, "kernel_us_from": kern_src,
+                     "launches_per_call": launches_per_call,
+                     "algorithmic_bytes_per_launch": algo_launch,
                      "algorithmic_bytes": algo_bytes,
                      "algorithmic_bytes_with_resample": algo_bytes + resample_bytes},
         "call_us": call_us,

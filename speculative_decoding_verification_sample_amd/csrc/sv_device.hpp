@@ -214,6 +214,30 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return lane63_u64(v);
 }
 
+// Inclusive prefix sums over a wave (lanes in order): shifts by 1, 2, 4 and
+// 8 inside each row of 16 lanes, then the row totals carried forward by the
+// row broadcasts.  Every lane must be active.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  auto bits = [](double x) { return (uint64_t)__double_as_longlong(x); };
+  auto val = [](uint64_t x) { return __longlong_as_double((long long)x); };
+  v += val(dpp_u64<0x111>(0, bits(v)));  // row_shr:1
+  v += val(dpp_u64<0x112>(0, bits(v)));  // row_shr:2
+  v += val(dpp_u64<0x114>(0, bits(v)));  // row_shr:4
+  v += val(dpp_u64<0x118>(0, bits(v)));  // row_shr:8
+  v += val(dpp_u64<kDppBcast15, 0xA>(0, bits(v)));
+  v += val(dpp_u64<kDppBcast31, 0xC>(0, bits(v)));
+  return v;
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += (int)dpp_u32<0x111>(0, (uint32_t)v);
+  v += (int)dpp_u32<0x112>(0, (uint32_t)v);
+  v += (int)dpp_u32<0x114>(0, (uint32_t)v);
+  v += (int)dpp_u32<0x118>(0, (uint32_t)v);
+  v += (int)dpp_u32<kDppBcast15, 0xA>(0, (uint32_t)v);
+  v += (int)dpp_u32<kDppBcast31, 0xC>(0, (uint32_t)v);
+  return v;
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // ---------------------------------------------------------------------------

@@ -438,21 +438,6 @@ __device__ __forceinline__ double block_sum(double v, double *red) {
   return s;
 }
 
-// Inclusive prefix sum over a wave (lanes in order): shifts by 1, 2, 4 and 8
-// inside each row of 16 lanes, then the row totals carried forward by the
-// row broadcasts.  Every lane must be active.
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  auto bits = [](double x) { return (uint64_t)__double_as_longlong(x); };
-  auto val = [](uint64_t x) { return __longlong_as_double((long long)x); };
-  v += val(dpp_u64<0x111>(0, bits(v)));  // row_shr:1
-  v += val(dpp_u64<0x112>(0, bits(v)));  // row_shr:2
-  v += val(dpp_u64<0x114>(0, bits(v)));  // row_shr:4
-  v += val(dpp_u64<0x118>(0, bits(v)));  // row_shr:8
-  v += val(dpp_u64<kDppBcast15, 0xA>(0, bits(v)));
-  v += val(dpp_u64<kDppBcast31, 0xC>(0, bits(v)));
-  return v;
-}
-
 // Cumulative masses of a split's entries from the start of the split: this
 // lane's entry ends at `incl` and starts at `prev`.
 struct SplitScan {

@@ -59,17 +59,6 @@ __device__ __forceinline__ int grid_bin(float x, float F, float kk) {
   return j < (float)kHistBins ? (int)j : kHistBins;
 }
 
-// inclusive prefix sum over the 64 lanes of a wave (fp64, shuffles)
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  const int l = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double u = __shfl_up(v, o, 64);
-    if (l >= o) v += u;
-  }
-  return v;
-}
-
 // Calls f(j, x) for every element of a row: 16-byte vector body, scalar
 // head / tail, four vectors in flight per lane.
 template <int DT, class F>
@@ -155,8 +144,8 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
   __shared__ unsigned cntf[kHistBins];
   __shared__ double wsum[2][kTopWaves];
   __shared__ float sM;
-  __shared__ double sZ;
-  __shared__ int s_fast, s_blo, s_bhi;
+  __shared__ double sZ, s_fu, s_fl;
+  __shared__ int s_fast, s_wbl[kTopWaves], s_wbh[kTopWaves];
 
   if (t < 64) {  // the streaming kernel has completed: every partial is in place
     float M = -INFINITY;
@@ -178,8 +167,12 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
       // and the grid positions are accurate to a small part of a bin
       s_fast = M > -INFINITY && fabsf(M * kk) < 262144.f && top_p < 1.0 &&
                (double)V * exp2(-(double)(kHistBins - 1) / kHistPerLog2) <= 0.5 * (1.0 - top_p) * Z;
-      s_blo = kHistBins;
-      s_bhi = kHistBins;
+      // the row's factors of the count bounds below: an element of bin J
+      // weighs between 2^-(J+phi)/64 and 2^-(J+phi-1)/64, phi = M kk -
+      // floor(M kk) (fp64 exponentials, once per row)
+      const float phi = M * kk - floorf(M * kk);
+      s_fu = exp2((double)(1.f - phi) / kHistPerLog2);
+      s_fl = exp2(-(double)phi / kHistPerLog2);
     }
   }
   __syncthreads();
@@ -218,22 +211,31 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
 
   // merge the splits' counts: split s's bin j is the row's bin j + off_s,
   // off_s = floor(M kk) - floor(m_s kk) >= 0.  Up to kMergeSplits splits at
-  // a time are staged in LDS by 16-byte loads; thread t then sums row bins
-  // t + 512 r over the staged splits, reading stage[s][J - off_s] (lanes
-  // read consecutive bytes: no bank conflicts, no atomics).  A saturated
-  // count (some bin of a split holds more than kCountSat elements) leaves
-  // the row to the fallback.
-  __shared__ uint32_t stage[kMergeSplits][kHistBins / 4];
+  // a time are staged in LDS by 16-byte loads, each split's counts behind a
+  // guard of zero words.  Thread t < kHistBins / 4 sums row bins 4t .. 4t+3:
+  // the four bytes at 4t - off_s of each staged split (one byte-align of the
+  // two words that hold them; bytes before the split's first bin come from
+  // its guard) are spread into two 16-bit lanes per word, even bins and odd
+  // bins, so that one add counts two bins (a group adds at most
+  // kMergeSplits * 255 per lane: no carries).  A saturated count (some bin
+  // of a split holds more than kCountSat elements) leaves the row to the
+  // fallback.
+  constexpr int kGuardW = 4;                          // 16 bytes: rows stay 16-byte aligned
+  constexpr int kRowW = kGuardW + kHistBins / 4 + 4;  // guard, counts, pad
+  __shared__ uint32_t stage[kMergeSplits][kRowW];
   __shared__ int s_off[kMergeSplits];
   __shared__ int s_sat;
   if (t == 0) s_sat = 0;
+  for (int i = t; i < kMergeSplits * 8; i += kTopThreads) {  // guards and pads
+    const int sp = i >> 3, q = i & 7;
+    stage[sp][q < 4 ? q : kRowW - 8 + q] = 0u;
+  }
   constexpr int kChunks = kHistBins / 16;  // 16-byte items per split
-  constexpr int kPer = kHistBins / kTopThreads;  // row bins per thread
+  constexpr int kPer = kHistBins / kTopThreads;  // row bins per thread in the bounds below
   constexpr int kStageIt = (kMergeSplits * kChunks + kTopThreads - 1) / kTopThreads;
   const uint8_t *h0 = a.part_h + (size_t)row * S * kHistBins;
-  unsigned acc[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) acc[r] = 0u;
+  const bool merger = t < kHistBins / 4;
+  unsigned acc[4] = {0u, 0u, 0u, 0u};
   bool sat = false;
   for (int g0 = 0; g0 < S; g0 += kMergeSplits) {
     const int gs = min(kMergeSplits, S - g0), items = gs * kChunks;
@@ -251,41 +253,53 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
     for (int u = 0; u < kStageIt; ++u) {
       const int i = t + u * kTopThreads;
       if (i < items) {
-        reinterpret_cast<u32x4 *>(&stage[0][0])[i] = v[u];
+        const int sp = i / kChunks, c = i - sp * kChunks;
+        *reinterpret_cast<u32x4 *>(&stage[sp][kGuardW + 4 * c]) = v[u];
 #pragma unroll
         for (int q = 0; q < 4; ++q)  // a byte 0xFF: a zero byte of ~w
           sat |= ((~v[u][q] - 0x01010101u) & v[u][q] & 0x80808080u) != 0u;
       }
     }
     __syncthreads();
-    for (int sp = 0; sp < gs; ++sp) {
-      const int off = s_off[sp];
-      if (off < 0) continue;
-      const uint8_t *hs = reinterpret_cast<const uint8_t *>(&stage[sp][0]);
-#pragma unroll
-      for (int r = 0; r < kPer; ++r) {
-        const int j = t + r * kTopThreads - off;
-        if (j >= 0) acc[r] += hs[j];
+    if (merger) {
+      uint32_t ev = 0u, od = 0u;  // 16-bit lanes: bins 4t, 4t+2 / 4t+1, 4t+3
+      for (int sp = 0; sp < gs; ++sp) {
+        const int off = s_off[sp];
+        const int o = 4 * t - off;  // the byte of row bin 4t in split sp
+        if (off < 0 || o <= -4) continue;
+        const int b = o + 4 * kGuardW;
+        const uint32_t x = __builtin_amdgcn_alignbyte(stage[sp][(b >> 2) + 1], stage[sp][b >> 2],
+                                                      (uint32_t)(b & 3));
+        ev += x & 0x00FF00FFu;
+        od += (x >> 8) & 0x00FF00FFu;
       }
+      acc[0] += ev & 0xFFFFu;
+      acc[1] += od & 0xFFFFu;
+      acc[2] += ev >> 16;
+      acc[3] += od >> 16;
     }
     __syncthreads();
   }
+  if (merger) {
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) cntf[t + r * kTopThreads] = acc[r];
+    for (int e = 0; e < 4; ++e) cntf[4 * t + e] = acc[e];
+  }
   if (sat) s_sat = 1;
   __syncthreads();
   // running upper / lower bounds of the mass from the top: b_lo = the first
   // bin where the upper bound reaches the goal, b_hi = the first where the
   // lower bound does
   {
-    const float phi = M * kk - F;  // in [0, 1)
+    // bin J's bounds: 2^-J/64 (one fp32 exponential per bin) times the
+    // row's two factors
+    const double fu = s_fu, fl = s_fl;
     double up[kPer], lo[kPer], su = 0.0, sl = 0.0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int bb = t * kPer + j;
-      const double c = (double)cntf[bb];
-      up[j] = c * (double)exp2f(-((float)bb + phi - 1.f) / kHistPerLog2);
-      lo[j] = c * (double)exp2f(-((float)bb + phi) / kHistPerLog2);
+      const double c = (double)cntf[bb] * (double)exp2f((float)bb * (-1.f / kHistPerLog2));
+      up[j] = c * fu;
+      lo[j] = c * fl;
       su += up[j];
       sl += lo[j];
     }
@@ -296,9 +310,12 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
     }
     __syncthreads();
     double cu = iu - su, cl = il - sl;
-    for (int u = 0; u < w; ++u) {
-      cu += wsum[0][u];
-      cl += wsum[1][u];
+#pragma unroll
+    for (int u = 0; u < kTopWaves; ++u) {
+      if (u < w) {
+        cu += wsum[0][u];
+        cl += wsum[1][u];
+      }
     }
     int bl = kHistBins, bh = kHistBins;
 #pragma unroll
@@ -308,19 +325,32 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_band(SampleArgs a) {
       if (bl == kHistBins && cu * (1.0 + kBoundSlack) >= goal) bl = t * kPer + j;
       if (bh == kHistBins && cl * (1.0 - kBoundSlack) >= goal) bh = t * kPer + j;
     }
-    if (bl < kHistBins) atomicMin(&s_blo, bl);
-    if (bh < kHistBins) atomicMin(&s_bhi, bh);
+    // thread t holds bins kPer t .. kPer t + kPer - 1, so the first bins
+    // are those of the lowest lane (of the lowest wave) that has them
+    const uint64_t hl = __ballot(bl < kHistBins), hh = __ballot(bh < kHistBins);
+    const int wl = hl ? __builtin_amdgcn_readlane(bl, (int)__builtin_ctzll(hl)) : kHistBins;
+    const int wh = hh ? __builtin_amdgcn_readlane(bh, (int)__builtin_ctzll(hh)) : kHistBins;
+    if ((t & 63) == 0) {
+      s_wbl[w] = wl;
+      s_wbh[w] = wh;
+    }
   }
   __syncthreads();
   if (t == 0) {
+    int blo = kHistBins, bhi = kHistBins;
+#pragma unroll
+    for (int u = 0; u < kTopWaves; ++u) {
+      blo = min(blo, s_wbl[u]);
+      bhi = min(bhi, s_wbh[u]);
+    }
     TopBand tb;
     tb.z = Z;
     tb.m = M;
     // the bound never reaching top_p would mean the counts missed mass:
     // the fallback decides such a row
-    tb.state = s_blo == kHistBins || s_sat ? kTopFallback : kTopCounts;
-    tb.blo = s_blo;
-    tb.bhi = s_bhi == kHistBins ? kHistBins - 1 : s_bhi;
+    tb.state = blo == kHistBins || s_sat ? kTopFallback : kTopCounts;
+    tb.blo = blo;
+    tb.bhi = bhi == kHistBins ? kHistBins - 1 : bhi;
     a.topband[row] = tb;
   }
 }
@@ -336,7 +366,7 @@ constexpr int kGRounds = kGWinEnt / (8 * kTopThreads);  // 16-byte loads of entr
 // 95, and the bf16 top-p call ran 577 -> 564 us at B256 K4 V152064)
 template <int DT>
 constexpr int gather_slots() { return DT == kBF16 ? 2 : 8; }
-constexpr int kGQueue = 256;     // vectors queued per wave before they are classified
+constexpr int kGQueue = 192;     // vectors queued per wave before they are classified
 constexpr int kGWaveKeys = 256;  // band keys a wave holds per pass
 
 // rank of the calling lane among the lanes set in `bal` below it
@@ -348,12 +378,7 @@ __device__ __forceinline__ unsigned lane_rank(uint64_t bal) {
 // workgroup; wtot is free again on return.
 __device__ __forceinline__ int block_excl_scan(int v, int *wtot, int *total) {
   const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (l >= o) incl += u;
-  }
+  const int incl = wave_incl_scan(v);
   if (l == 63) wtot[w] = incl;
   __syncthreads();
   int before = incl - v, sum = 0;
@@ -376,7 +401,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *wtot, int *total) {
 // and tail elements are visited too.  The row's keys go to its list at
 // offsets from a workgroup scan, with no atomics.
 template <int DT>
-__global__ __launch_bounds__(kTopThreads) void k_topp_gather(SampleArgs a) {
+__global__ __launch_bounds__(kTopThreads, 6) void k_topp_gather(SampleArgs a) {
   const int row = blockIdx.x, S = a.S, t = threadIdx.x;
   const TopRow tr = top_row<DT>(a, row);
   if (tr.q.invalid || tr.q.greedy || !(tr.q.top_p < 1.0)) return;
@@ -561,7 +586,7 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_gather(SampleArgs a) {
 // cut: per row, the radix rounds (and the fallback for uncovered rows)
 // ---------------------------------------------------------------------------
 template <int DT>
-__global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
+__global__ __launch_bounds__(kTopThreads, 8) void k_topp_cut(SampleArgs a) {
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int w = t >> 6;
@@ -715,17 +740,13 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
   // order), and the rows are summed in wave order, so the kept mass is the
   // same bit for bit on every run; the counts and key bounds are integers.
   __shared__ double exc[kBins], rtot[kBins / 64];
-  __shared__ int s_first, s_lastnz;
+  __shared__ int s_wfirst[kBins / 64], s_wlast[kBins / 64];
   for (int shift = shift0; shift >= 0 && !s_done; shift -= 8) {
     for (int i = t; i < kTopWaves * kBins; i += kTopThreads) (&hist[0][0])[i] = 0.0;
     if (t < kBins) {
       cnt[t] = 0;
       kmin[t] = 0xFFFFFFFFu;
       kmax[t] = 0u;
-    }
-    if (t == 0) {
-      s_first = kBins;
-      s_lastnz = -1;
     }
     __syncthreads();
     const unsigned prefix = s_prefix;
@@ -770,16 +791,31 @@ __global__ __launch_bounds__(kTopThreads) void k_topp_cut(SampleArgs a) {
     const double incl = wave_incl_scan(v);
     if (t < kBins && (t & 63) == 63) rtot[t >> 6] = incl;
     __syncthreads();
+    bool reach = false;
     if (t < kBins) {
       double ex = incl - v;
-      for (int u = 0; u < (t >> 6); ++u) ex += rtot[u];
+#pragma unroll
+      for (int u = 0; u < kBins / 64; ++u)
+        if (u < (t >> 6)) ex += rtot[u];
       exc[t] = ex;
-      if (nz && s_above + ex + v >= goal) atomicMin(&s_first, t);
-      if (nz) atomicMax(&s_lastnz, t);
+      reach = nz && s_above + ex + v >= goal;
+    }
+    // the first lane that reaches the goal and the last non-empty one, per
+    // wave (lanes ascend with t)
+    const uint64_t hr = __ballot(reach), hn = __ballot(nz);
+    if (t < kBins && (t & 63) == 0) {
+      s_wfirst[w] = hr ? (t & ~63) + (int)__builtin_ctzll(hr) : kBins;
+      s_wlast[w] = hn ? (t & ~63) + 63 - (int)__builtin_clzll(hn) : -1;
     }
     __syncthreads();
     if (t == 0) {
-      const int pt = s_first < kBins ? s_first : s_lastnz;
+      int first = kBins, lastnz = -1;
+#pragma unroll
+      for (int u = 0; u < kBins / 64; ++u) {
+        first = min(first, s_wfirst[u]);
+        lastnz = max(lastnz, s_wlast[u]);
+      }
+      const int pt = first < kBins ? first : lastnz;
       if (pt < 0) {  // nothing gathered: cannot happen; keep everything
         s_done = 1;
         s_tau = -INFINITY;
