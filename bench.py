@@ -112,7 +112,7 @@ def main():
                          "merge: two drafters' trees merged with confidence routing; "
                          "lmhead: greedy verify with the LM head fused in front")
     ap.add_argument("--sets", type=int, default=3,
-                    help="input sets rotated across steps (1 when one set is >= 512 MiB)")
+                    help="input sets rotated across steps (2 when one set is >= 512 MiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -152,7 +152,10 @@ def main():
         log(f"input set {s}: {w.name} generated in {time.time() - t0:.1f}s")
         sets.append(w)
         if w.logit_bytes >= 2 * MALL_BYTES:
-            n_sets = 1  # one set already overflows the memory-side cache twice
+            # a set that overflows the memory-side cache twice: two sets, so
+            # that what one call leaves in that cache (the last lines it
+            # read) is not the next call's input
+            n_sets = min(n_sets, 2)
         s += 1
     w0 = sets[0]
 

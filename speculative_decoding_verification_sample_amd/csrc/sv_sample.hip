@@ -993,6 +993,36 @@ hipError_t launch_topp_decide(const SampleArgs &a, hipStream_t stream) {
 // workgroup waits for another: the launch streams at the memory's pace.
 constexpr int kMassSplits = 2;  // residual splits per workgroup of the mass launch
 
+// Whether this lane's body groups of a residual split can hold an element of
+// the target row's nucleus (logit >= tau): p' is 0 below tau, and so is the
+// residual max(0, p' - q').  The lane's kVecPerThreadB groups lie in one
+// 128-byte line of a streaming split (residual and streaming splits start
+// at multiples of 16 KB, so both share the row's 16-byte phase, and lines are
+// aligned runs of eight groups); the streaming pass recorded that line's
+// maximum, rounded up, in part_c (entry g * 8 + u for the groups 8 g .. 8 g
+// + 7 of slot u, i.e. body groups u kThreads + 8 g .. + 7).  Groups that no
+// recorded line covers (a streaming split's scalar tail and head) are always
+// loaded.
+template <int DT>
+__device__ __forceinline__ bool lane_in_nucleus(const SplitGeo &g, const char *rt, int V,
+                                                const uint16_t *cm_row, float tau) {
+  constexpr int EPV = 16 / elem_bytes(DT);
+  constexpr int VB = kVecPerThreadB;
+  static_assert(8 % VB == 0 && kChunkLanes == 8, "a lane's groups lie in one line");
+  const int v0 = threadIdx.x * VB;
+  if (v0 >= g.nvec) return false;  // past the body: never counted
+  const int e = g.e0 + g.head + v0 * EPV;  // the row element that starts the lane's groups
+  const int s = e / split_elems(DT);
+  const Span sp = split_span(rt, V, s, DT);
+  const int off = e - sp.e0 - sp.head;
+  if (off < 0 || off % EPV != 0) return true;
+  const int vb = off / EPV;
+  if (vb % VB != 0 || vb + VB > sp.nvec) return true;
+  const int entry = ((vb % kThreads) / kChunkLanes) * kChunkLanes + vb / kThreads;
+  const uint32_t c = cm_row[(size_t)s * kChunksPerSplit + entry];
+  return !(__uint_as_float(c << 16) < tau);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_resid_mass(SampleArgs a) {
   __shared__ double red[kThreads / 64];
@@ -1002,15 +1032,30 @@ __global__ __launch_bounds__(kThreads) void k_resid_mass(SampleArgs a) {
   const int s0 = ((int)blockIdx.x - b * per_req) * kMassSplits;
   const Decision d = a.dec[b];
   if (d.n < 0) return;
-  const char *rt = row_ptr(a.target, (size_t)b * (a.K + 1) + d.n, a.V, DT);
+  const size_t trow = (size_t)b * (a.K + 1) + d.n;
+  const char *rt = row_ptr(a.target, trow, a.V, DT);
   const char *rd = d.mode == kModeResidual ? row_ptr(a.draft, (size_t)b * a.K + d.n, a.V, DT) : rt;
-  // every split's loads issued before any is used
+  // only lines of the target row that can reach its nucleus are read (both
+  // rows); the rest holds no residual mass.  Every split's loads issued
+  // before any is used.
+  const uint16_t *cm_row = a.part_c ? a.part_c + trow * a.S * kChunksPerSplit : nullptr;
+  const bool skip = cm_row && d.tau_t > -INFINITY;
   SplitGeo g[kMassSplits];
-  LaneGroups mine[kMassSplits];
+  bool need[kMassSplits];
 #pragma unroll
   for (int j = 0; j < kMassSplits; ++j) {
     g[j] = split_geo<DT>(rt, rd, a.V, min(s0 + j, a.SB - 1));
-    load_lane<DT, false>(g[j], mine[j]);
+    need[j] = !skip || !g[j].aligned || lane_in_nucleus<DT>(g[j], rt, a.V, cm_row, d.tau_t);
+  }
+  LaneGroups mine[kMassSplits];
+#pragma unroll
+  for (int j = 0; j < kMassSplits; ++j) {
+    if (need[j]) {
+      load_lane<DT, false>(g[j], mine[j]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kVecPerThreadB; ++u) mine[j].wt[u] = mine[j].wq[u] = neg_inf_vec<DT>();
+    }
   }
   if (threadIdx.x < kMassSplits && s0 + (int)threadIdx.x < a.SB) {
     const int j = threadIdx.x;
