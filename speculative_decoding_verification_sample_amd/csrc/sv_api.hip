@@ -169,7 +169,8 @@ int run_sample(const void *target_logits, const void *draft_logits, int dtype,
   a.rowstat = use_top_p ? carve<sv::RowStat>(workspace, L.rowstat) : nullptr;
   a.rtot = carve<sv::u64>(workspace, L.rtot);
   a.part_h = use_top_p ? carve<uint8_t>(workspace, L.part_h) : nullptr;
-  a.part_c = use_top_p ? carve<uint16_t>(workspace, L.part_c) : nullptr;
+  a.part_c = use_top_p ? carve<uint32_t>(workspace, L.part_c) : nullptr;
+  a.part_c2 = use_top_p ? carve<uint16_t>(workspace, L.part_c2) : nullptr;
   a.topband = use_top_p ? carve<sv::TopBand>(workspace, L.topband) : nullptr;
   a.band_n = use_top_p ? carve<unsigned>(workspace, L.band_n) : nullptr;
   a.band_keys = use_top_p ? carve<uint32_t>(workspace, L.band_keys) : nullptr;

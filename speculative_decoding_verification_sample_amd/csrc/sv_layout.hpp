@@ -103,11 +103,13 @@ constexpr float kHistPerLog2 = 64.f;
 constexpr unsigned kCountSat = 255u;
 // Top-p: keys of a row's band kept for the cut (more: the cut reads the row).
 constexpr int kBandKeys = 4096;
-// Top-p: a streaming tile also records each chunk's maximum, a chunk being
-// one vector slot u of a group g of eight consecutive lanes (8 x 16 bytes:
-// one 128-byte line), as the upper half of the fp32 pattern rounded so the
-// value it denotes is not below the maximum.  Entry g * kVecPerThread + u:
-// lane t writes entry t, and a lane reads its slots' entries in one load.
+// Top-p: a streaming tile also records, per chunk, the chunk's maximum
+// exactly (its fp32 pattern) and a bound on its second largest element (the
+// upper half of that element's fp32 pattern, rounded so the value it denotes
+// is not below the element), a chunk being one vector slot u of a group g of
+// eight consecutive lanes (8 x 16 bytes: one 128-byte line).  Entry g *
+// kVecPerThread + u: lane t writes entry t, and a lane reads its slots'
+// entries in one load.
 constexpr int kChunkLanes = 8;
 constexpr int kChunksPerSplit = kThreads * kVecPerThread / kChunkLanes;
 static_assert(kChunkLanes == kVecPerThread, "lane t writes entry t");
@@ -140,7 +142,8 @@ struct SampleArgs {
   RowStat *rowstat;
   u64 *rtot;  // per (request, residual split): the split's mass as two tagged fp32 words
   uint8_t *part_h;  // top-p: per (row, split) kHistBins element counts (null otherwise)
-  uint16_t *part_c;  // top-p: per (row, split) kChunksPerSplit chunk maxima
+  uint32_t *part_c;   // top-p: per (row, split) kChunksPerSplit chunk maxima (fp32 patterns)
+  uint16_t *part_c2;  // top-p: per (row, split) kChunksPerSplit bounds on the chunks' second largest elements
   TopBand *topband;  // top-p: per row
   unsigned *band_n;  // top-p: per row, keys in the band (the list holds the first kBandKeys)
   uint32_t *band_keys;  // top-p: per row, kBandKeys keys
@@ -193,7 +196,8 @@ struct Layout {
   int SB = 0;      // residual splits per row (sampling)
   int rows = 0;    // logit rows streamed
   size_t part_m = 0, part_z = 0, part_x = 0, part_key = 0, part_tag = 0, rowstat = 0;
-  size_t rtot = 0, part_h = 0, part_c = 0, topband = 0, band_n = 0, band_keys = 0, band_above = 0;
+  size_t rtot = 0, part_h = 0, part_c = 0, part_c2 = 0, topband = 0, band_n = 0, band_keys = 0,
+         band_above = 0;
   size_t dec = 0;
   // sampling: part_m one self-validating u64 word per (row, split) (the split
   // maximum), part_z two (the split mass as fp32 hi + lo);
@@ -230,7 +234,8 @@ inline Layout make_layout(int op, int B, int KN, int V, int dtype, int use_top_p
     L.rtot = take((size_t)B * (size_t)L.SB * 2 * sizeof(u64));
     if (use_top_p) {
       L.part_h = take(cells * kHistBins * sizeof(uint8_t));
-      L.part_c = take(cells * kChunksPerSplit * sizeof(uint16_t));
+      L.part_c = take(cells * kChunksPerSplit * sizeof(uint32_t));
+      L.part_c2 = take(cells * kChunksPerSplit * sizeof(uint16_t));
       L.topband = take((size_t)L.rows * sizeof(TopBand));
       L.band_n = take((size_t)L.rows * sizeof(unsigned));
       L.band_keys = take((size_t)L.rows * kBandKeys * sizeof(uint32_t));

@@ -924,7 +924,8 @@ __global__ __launch_bounds__(kThreads) void k_sample_fused(
           w = *(const_u32p)(ea - mis);
         }
       }
-    }, hist, hist ? a.part_c + ((size_t)grow * S + s) * kChunksPerSplit : nullptr);
+    }, hist, hist ? a.part_c + ((size_t)grow * S + s) * kChunksPerSplit : nullptr,
+       hist ? a.part_c2 + ((size_t)grow * S + s) * kChunksPerSplit : nullptr);
     if (threadIdx.x == 0) {
       const size_t g = (size_t)grow * S + s;
       float zh, zl;
@@ -999,13 +1000,13 @@ constexpr int kMassSplits = 2;  // residual splits per workgroup of the mass lau
 // 128-byte line of a streaming split (residual and streaming splits start
 // at multiples of 16 KB, so both share the row's 16-byte phase, and lines are
 // aligned runs of eight groups); the streaming pass recorded that line's
-// maximum, rounded up, in part_c (entry g * 8 + u for the groups 8 g .. 8 g
+// maximum in part_c (entry g * 8 + u for the groups 8 g .. 8 g
 // + 7 of slot u, i.e. body groups u kThreads + 8 g .. + 7).  Groups that no
 // recorded line covers (a streaming split's scalar tail and head) are always
 // loaded.
 template <int DT>
 __device__ __forceinline__ bool lane_in_nucleus(const SplitGeo &g, const char *rt, int V,
-                                                const uint16_t *cm_row, float tau) {
+                                                const uint32_t *cm_row, float tau) {
   constexpr int EPV = 16 / elem_bytes(DT);
   constexpr int VB = kVecPerThreadB;
   static_assert(8 % VB == 0 && kChunkLanes == 8, "a lane's groups lie in one line");
@@ -1019,8 +1020,7 @@ __device__ __forceinline__ bool lane_in_nucleus(const SplitGeo &g, const char *r
   const int vb = off / EPV;
   if (vb % VB != 0 || vb + VB > sp.nvec) return true;
   const int entry = ((vb % kThreads) / kChunkLanes) * kChunkLanes + vb / kThreads;
-  const uint32_t c = cm_row[(size_t)s * kChunksPerSplit + entry];
-  return !(__uint_as_float(c << 16) < tau);
+  return !(__uint_as_float(cm_row[(size_t)s * kChunksPerSplit + entry]) < tau);
 }
 
 template <int DT>
@@ -1038,7 +1038,7 @@ __global__ __launch_bounds__(kThreads) void k_resid_mass(SampleArgs a) {
   // only lines of the target row that can reach its nucleus are read (both
   // rows); the rest holds no residual mass.  Every split's loads issued
   // before any is used.
-  const uint16_t *cm_row = a.part_c ? a.part_c + trow * a.S * kChunksPerSplit : nullptr;
+  const uint32_t *cm_row = a.part_c ? a.part_c + trow * a.S * kChunksPerSplit : nullptr;
   const bool skip = cm_row && d.tau_t > -INFINITY;
   SplitGeo g[kMassSplits];
   bool need[kMassSplits];

@@ -21,12 +21,13 @@ __device__ __forceinline__ u32x4 neg_inf_vec() {
 // floor(l kk), kk = k * kHistPerLog2 (bins of 1/64 log2 unit on a grid shared
 // by all splits, so that counts merge across splits by integer offsets);
 // bins past kHistBins are not counted.  With `hist`, `cmax` takes the
-// split's chunk maxima (kChunksPerSplit entries, f32_hi_up of each).  HIST
-// false compiles neither (both pointers are then ignored).
+// split's chunk maxima (kChunksPerSplit entries, fp32 patterns) and `cmax2`
+// a bound on each chunk's second largest element (f32_hi_up of it).  HIST
+// false compiles none of it (the pointers are then ignored).
 template <int DT, bool HIST, class Pre>
 __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale k, float *M_out,
                                              double *Z_out, Pre &&pre, uint8_t *hist,
-                                             uint16_t *cmax) {
+                                             uint32_t *cmax, uint16_t *cmax2) {
   constexpr int EPV = 16 / elem_bytes(DT);
   const Span sp = split_span(rp, V, s, DT);
   const u32x4 *body = span_body(sp, DT);
@@ -50,14 +51,27 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
   const float xs = se >= 0 ? load_elem(sp.base, se, DT) : -INFINITY;
   pre();
 
+  // HIST: each slot's largest and second largest element over the lane's
+  // elements (the second by a median of three: med3(first, second, x) is
+  // the new second whenever first >= second).  fp32 slots (four elements)
+  // take them here, in place of the plain maximum; bf16 slots (eight, each
+  // widened here and again below) take them in the exponential pass, where
+  // each widened element is at hand (here they would keep all 64 widened
+  // elements live: 149 registers instead of 93).
+  constexpr bool kTop2First = DT == kF32;
   float m = xs;
-  float mu[kVecPerThread];  // HIST: each slot's maximum over the lane's elements
-  if constexpr (HIST) {
+  float mu[kVecPerThread], mv[kVecPerThread];
+  if constexpr (HIST && kTop2First) {
 #pragma unroll
     for (int u = 0; u < kVecPerThread; ++u) {
       mu[u] = vec_elem(buf[u], 0, DT);
+      mv[u] = -INFINITY;
 #pragma unroll
-      for (int e = 1; e < EPV; ++e) mu[u] = fmaxf(mu[u], vec_elem(buf[u], e, DT));
+      for (int e = 1; e < EPV; ++e) {
+        const float x = vec_elem(buf[u], e, DT);
+        mv[u] = __builtin_amdgcn_fmed3f(mu[u], mv[u], x);
+        mu[u] = fmaxf(mu[u], x);
+      }
       m = fmaxf(m, mu[u]);
     }
   } else {
@@ -65,6 +79,10 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
     for (int u = 0; u < kVecPerThread; ++u)
 #pragma unroll
       for (int e = 0; e < EPV; ++e) m = fmaxf(m, vec_elem(buf[u], e, DT));
+    if constexpr (HIST) {
+#pragma unroll
+      for (int u = 0; u < kVecPerThread; ++u) mu[u] = mv[u] = -INFINITY;
+    }
   }
 
   // 2^((l - m) k) with k = hi + lo: the exponent is taken as
@@ -89,6 +107,14 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
         a1 += term(j + 1);
       }
       z += (double)(a0 + a1);
+      if constexpr (HIST && !kTop2First) {
+#pragma unroll
+        for (int j = 0; j < EPV; ++j) {
+          const float x = vec_elem(buf[u], j, DT);
+          mv[u] = __builtin_amdgcn_fmed3f(mu[u], mv[u], x);
+          mu[u] = fmaxf(mu[u], x);
+        }
+      }
     }
     if (se >= 0) z += (double)exp2_fast(fmaf(xs, k.lo, fmaf(xs, k.hi, c)));
     // 2^delta for |delta| < 1e-5: 1 + delta ln2 + (delta ln2)^2 / 2, error < 1e-16
@@ -109,27 +135,46 @@ __device__ __forceinline__ void softmax_tile(const char *rp, int V, int s, Scale
   }
   __syncthreads();
   if (HIST && hist) {
-    // chunk maxima: slot u's lane maxima, reduced over the group of eight
-    // lanes by a reduce-scatter of three exchanges (partner 7 - i, i ^ 2,
-    // i ^ 1), each lane keeping the half of its slots whose index bit
-    // matches its own lane bit and sending the other half: lane t ends with
-    // the maximum of slot t % 8
+    // chunk maxima and second elements: slot u's lane pairs (largest,
+    // second), reduced over the group of eight lanes by a reduce-scatter of
+    // three exchanges (partner 7 - i, i ^ 2, i ^ 1), each lane keeping the
+    // half of its slots whose index bit matches its own lane bit and sending
+    // the other half: lane t ends with slot t % 8's pair.  Two pairs merge
+    // as (max of the firsts, max(min of the firsts, max of the seconds)).
     const uint32_t ninf = __float_as_uint(-INFINITY);
     const int li = t & (kChunkLanes - 1);
-    float c4[4], c2[2];
+    auto merge = [](float &a1, float &a2, float b1, float b2) {
+      a2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+      a1 = fmaxf(a1, b1);
+    };
+    float p4[4], q4[4], p2[2], q2[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float keep = li & 4 ? mu[j + 4] : mu[j], send = li & 4 ? mu[j] : mu[j + 4];
-      c4[j] = fmaxf(keep, __uint_as_float(dpp_u32<kDppHalfMirror>(ninf, __float_as_uint(send))));
+      const bool hi = li & 4;
+      p4[j] = hi ? mu[j + 4] : mu[j];
+      q4[j] = hi ? mv[j + 4] : mv[j];
+      const float s1 = hi ? mu[j] : mu[j + 4], s2 = hi ? mv[j] : mv[j + 4];
+      merge(p4[j], q4[j], __uint_as_float(dpp_u32<kDppHalfMirror>(ninf, __float_as_uint(s1))),
+            __uint_as_float(dpp_u32<kDppHalfMirror>(ninf, __float_as_uint(s2))));
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const float keep = li & 2 ? c4[j + 2] : c4[j], send = li & 2 ? c4[j] : c4[j + 2];
-      c2[j] = fmaxf(keep, __uint_as_float(dpp_u32<kDppXor2>(ninf, __float_as_uint(send))));
+      const bool hi = li & 2;
+      p2[j] = hi ? p4[j + 2] : p4[j];
+      q2[j] = hi ? q4[j + 2] : q4[j];
+      const float s1 = hi ? p4[j] : p4[j + 2], s2 = hi ? q4[j] : q4[j + 2];
+      merge(p2[j], q2[j], __uint_as_float(dpp_u32<kDppXor2>(ninf, __float_as_uint(s1))),
+            __uint_as_float(dpp_u32<kDppXor2>(ninf, __float_as_uint(s2))));
     }
-    const float keep = li & 1 ? c2[1] : c2[0], send = li & 1 ? c2[0] : c2[1];
-    const float got = __uint_as_float(dpp_u32<kDppXor1>(ninf, __float_as_uint(send)));
-    cmax[t] = (uint16_t)f32_hi_up(fmaxf(keep, got));
+    {
+      const bool hi = li & 1;
+      float p1 = hi ? p2[1] : p2[0], q1 = hi ? q2[1] : q2[0];
+      const float s1 = hi ? p2[0] : p2[1], s2 = hi ? q2[0] : q2[1];
+      merge(p1, q1, __uint_as_float(dpp_u32<kDppXor1>(ninf, __float_as_uint(s1))),
+            __uint_as_float(dpp_u32<kDppXor1>(ninf, __float_as_uint(s2))));
+      cmax[t] = __float_as_uint(p1);
+      cmax2[t] = (uint16_t)f32_hi_up(q1);
+    }
     float M = sm[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, sm[w]);

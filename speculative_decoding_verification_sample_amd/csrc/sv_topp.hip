@@ -17,8 +17,10 @@
 //     under half of the mass top_p leaves out, so the cut lies inside.
 //   gather (one workgroup per row): the exact mass of the row's elements
 //     nearer than the band, and the band's elements as order-preserving
-//     value keys in a per-row list; the streaming pass's chunk maxima let
-//     it read only the 128-byte lines that can hold such elements.
+//     value keys in a per-row list; the streaming pass's record of each
+//     128-byte line (its maximum, exactly, and a bound on its second
+//     element) gives the lines with one such element without a read, and
+//     only the lines with two or more are read.
 //   cut (one workgroup per row): radix rounds of 8 bits over the keys,
 //     accumulating mass from the top, until one distinct value remains:
 //     that value is tau, the mass at or above it is the kept mass.
@@ -392,14 +394,17 @@ __device__ __forceinline__ int block_excl_scan(int v, int *wtot, int *total) {
   return before;
 }
 
-// One workgroup per row, over windows of kGWin splits: the window's chunk
-// maxima pick the 128-byte lines that can hold an element at or above the
-// band (a chunk whose rounded-up maximum c has c kk < F - bhi holds none:
-// x <= c and kk > 0 give x kk <= c kk, rounding keeps the order); their
-// indices are packed into LDS, and passes of kGPerPass lines, each line read
-// by a group of eight lanes, visit only those.  Every split's scalar head
-// and tail elements are visited too.  The row's keys go to its list at
-// offsets from a workgroup scan, with no atomics.
+// One workgroup per row, over windows of kGWin splits.  The window's chunk
+// records classify the 128-byte lines: a chunk whose maximum c has c kk <
+// F - bhi holds no element at or above the band (x <= c and kk > 0 give x
+// kk <= c kk, rounding keeps the order); a chunk whose second largest
+// element lies below the band holds exactly one, its maximum, which the
+// record gives exactly; only the remaining chunks are read: their indices
+// are packed into LDS, and passes of kGPerPass lines, each line read by a
+// group of eight lanes, visit only those.  Every split's scalar head and
+// tail elements are visited too.  Each wave appends its band keys in a
+// fixed order, and the waves' lists go to the row's list in wave order,
+// with no atomics.
 template <int DT>
 __global__ __launch_bounds__(kTopThreads, 6) void k_topp_gather(SampleArgs a) {
   const int row = blockIdx.x, S = a.S, t = threadIdx.x;
@@ -426,7 +431,8 @@ __global__ __launch_bounds__(kTopThreads, 6) void k_topp_gather(SampleArgs a) {
   __shared__ int gkn[kTopWaves];
   const int w = t >> 6, lane = t & 63;
   uint32_t *keys = a.band_keys + (size_t)row * kBandKeys;
-  const uint16_t *cm = a.part_c + (size_t)row * S * kChunksPerSplit;
+  const uint32_t *cm = a.part_c + (size_t)row * S * kChunksPerSplit;
+  const uint16_t *cm2 = a.part_c2 + (size_t)row * S * kChunksPerSplit;
   double above = 0.0;
   int kbase = 0;  // keys of the passes before (uniform)
   int kn = 0;     // the wave's band keys in this pass (uniform in the wave)
@@ -439,13 +445,21 @@ __global__ __launch_bounds__(kTopThreads, 6) void k_topp_gather(SampleArgs a) {
 
   for (int s0 = 0; s0 < S; s0 += kGWin) {
     const int sw = min(kGWin, S - s0), nent = sw * kChunksPerSplit;
-    // the window's chunk maxima, eight entries a lane and round ...
-    u32x4 cw[kGRounds];
+    // the window's chunk maxima and second-element bounds, eight entries a
+    // lane and round ...
+    u32x4 c1w[kGRounds][2], c2w[kGRounds];
 #pragma unroll
     for (int r = 0; r < kGRounds; ++r) {
       const int e = (r * kTopThreads + t) * 8;
-      cw[r] = e < nent ? *reinterpret_cast<const u32x4 *>(cm + (size_t)s0 * kChunksPerSplit + e)
-                       : neg_inf_vec<kBF16>();
+      if (e < nent) {
+        const size_t at = (size_t)s0 * kChunksPerSplit + e;
+        c1w[r][0] = *reinterpret_cast<const u32x4 *>(cm + at);
+        c1w[r][1] = *reinterpret_cast<const u32x4 *>(cm + at + 4);
+        c2w[r] = *reinterpret_cast<const u32x4 *>(cm2 + at);
+      } else {
+        c1w[r][0] = c1w[r][1] = neg_inf_vec<kF32>();
+        c2w[r] = neg_inf_vec<kBF16>();
+      }
     }
     // ... and each split's scalars (lanes 16 j .. 16 j + 15 for split s0 + j)
     float xs = -INFINITY;
@@ -457,7 +471,12 @@ __global__ __launch_bounds__(kTopThreads, 6) void k_topp_gather(SampleArgs a) {
         if (se >= 0) xs = load_elem(sp.base, se, DT);
       }
     }
-    // the needed entries, packed into the list
+    // A line holds an element at or above the band iff its maximum c1 does.
+    // If its second largest element lies below the band, c1 is the only
+    // one, and its value (recorded exactly) is all the band needs: its mass
+    // if above the band, else its key (appended to the wave's key list in
+    // lane order), with no read of the line.  Only lines with two or more
+    // such elements (about one in fifty) go into the list.
     uint32_t bits[kGRounds];
     int cnt = 0;
 #pragma unroll
@@ -465,8 +484,19 @@ __global__ __launch_bounds__(kTopThreads, 6) void k_topp_gather(SampleArgs a) {
       bits[r] = 0u;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t h = (cw[r][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-        bits[r] |= !(__uint_as_float(h << 16) * kk < yb) ? 1u << j : 0u;
+        const float c1 = __uint_as_float(c1w[r][j >> 2][j & 3]);
+        const float c2 = __uint_as_float(((c2w[r][j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << 16);
+        const float y1 = c1 * kk;
+        const bool cand = y1 >= yb;
+        const bool many = cand && !(c2 * kk < yb);
+        bits[r] |= many ? 1u << j : 0u;
+        const bool one = cand && !many;
+        if (one && y1 >= ya) above += (double)tempered(c1, M, k);
+        const bool inb = one && y1 < ya;
+        const uint64_t bal = __ballot(inb);
+        const int kp = kn + (int)lane_rank(bal);
+        if (inb && kp < kGWaveKeys) gkeys[w][kp] = key_of_f32(c1);
+        kn += __popcll(bal);
       }
       cnt += __builtin_popcount(bits[r]);
     }
