@@ -255,6 +255,31 @@ def test_topp_many_splits():
         _check(w, offset=1)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T,top_p", [
+    (0.02, 1.0),      # nearly one-hot rows
+    (0.02, 0.9),
+    (50.0, 1.0),      # nearly flat rows
+    (50.0, 0.9),      # the nucleus holds most of the row
+    (1.0, 1e-4),      # only the largest value's tie group is kept
+    (1.0, 0.999),     # the nucleus reaches far down the row
+])
+def test_extreme_temperature_and_top_p(dtype, T, top_p):
+    """Temperatures far from 1 and top_p at both ends, each request's
+    outcome, p', q' and residual mass against the oracle."""
+    rng = np.random.default_rng(int(T * 100) + int(top_p * 1e4))
+    B, K, V = 4, 3, 40009
+    t32 = rng.normal(0, 2.5, (B, K + 1, V)).astype(np.float32)
+    d32 = (t32[:, :K] + rng.normal(0, 1, (B, K, V))).astype(np.float32)
+    target, draft = W._to_dtype(t32, dtype), W._to_dtype(d32, dtype)
+    tf = float(np.float32(T))
+    tp = float(np.float32(top_p))
+    toks = W.drafter_tokens(W.logits_as_f32(draft, dtype), tf, tp, rng)
+    w = W.Workload("sample", f"T={T} top_p={top_p} {dtype}", B, K, V, dtype, target, draft, toks,
+                   W.uniforms_on_grid(rng, (B, K)), W.uniforms_on_grid(rng, (B,)), tf, tp)
+    _check(w, offset=1)
+
+
 def test_flat_rows_and_neg_inf():
     rng = np.random.default_rng(4)
     B, K, V = 4, 3, 3000
