@@ -143,6 +143,21 @@ def test_max_sizes_k63_n64():
     assert (ref["path_len"] == N - 1).all()
 
 
+def test_many_requests_short_rows():
+    """Thousands of requests over short rows: grids far larger than the
+    device holds at once (the residual tiles' lag, every request's tiles and
+    hand-offs), sampling with and without top-p, greedy and tree."""
+    w = W.sample_gaussian(17, 2048, 4, 1000, "f32", 2.0, 0.5, 0.8, name="many")
+    _check(w)
+    wp = W.sample_gaussian(18, 1536, 3, 1500, "bf16", 2.0, 0.5, 0.8, name="many-topp")
+    wp.top_p = float(np.float32(0.9))
+    _check(wp)
+    g = W.greedy_gaussian(19, 4096, 5, 600, "bf16", agree=0.8, name="many-greedy")
+    _check(g)
+    t = W.tree_merged(20, 512, 7, 900, "f32", name="many-tree")
+    _check(t)
+
+
 # ---------------------------------------------------------------------------
 # ties, -inf entries, degenerate distributions
 # ---------------------------------------------------------------------------
