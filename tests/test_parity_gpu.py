@@ -84,6 +84,17 @@ def test_full_c4_shape_bf16_topp_all_requests():
     _check(w, max_flagged_share=0.01)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_full_vocabulary_topp_misaligned_rows(dtype):
+    """The top-p setting at V = 152064 with every row starting one element
+    past a 16-byte boundary: scalar heads and tails in every split of the
+    streaming, gather, cut and residual passes, line records shifted by the
+    row's phase."""
+    w = W.sample_zipf_topp(3, 24, 4, 152064, 0.8, 0.95, seed=5, name=f"c4-shaped {dtype} misaligned",
+                           dtype=dtype)
+    _check(w, offset=1, max_flagged_share=0.1)
+
+
 def test_full_c3_high_acceptance():
     """Draft = target + N(0, 0.05^2): nearly every draft survives and the
     residual mass S of a rejection is small (a few hundredths), where a
