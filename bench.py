@@ -131,7 +131,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on one GPU only (--gpus {args.gpus} requested); "
-              "the verify step shards over requests with no exchange, see the design notes.",
+              "the verify step shards over requests, with no exchange between GPUs.",
               file=sys.stderr)
         sys.exit(2)
 
